@@ -1,0 +1,209 @@
+/*
+ * growpage.h - C ABI of the GrowPage capacity-boundary event on MI355X.
+ *
+ * GrowPage ("GrowPage: On-Demand KV Budgeting for Efficient LLM Reasoning
+ * Serving", arXiv 2609.03494) decides at each KV capacity boundary of a
+ * request whether to compress its cache in place ("Compress & Hold") or to
+ * take one more physical page ("Grow by One Page").  This library runs that
+ * boundary event on the GPU for a batch of requests over a paged KV cache.
+ * Section, equation and appendix numbers below refer to that paper.
+ *
+ * Conventions
+ *  - Ownership: the caller allocates and owns every buffer (device pool,
+ *    query-state pool, block tables, free-page stack, workspace, outputs)
+ *    and the stream.  The library borrows raw pointers for the duration of
+ *    the enqueue.  gp_create allocates a few bytes of device memory for
+ *    counters and an error word; no other call allocates.
+ *  - Asynchrony: every gp_* call that takes a stream enqueues kernels on it
+ *    and returns after host-side validation; results are valid once the
+ *    stream has reached that point.  No call synchronises the device except
+ *    gp_get_counters and gp_get_device_errors.
+ *  - Errors: host-checkable problems return an error status and enqueue
+ *    nothing.  Device-side checks (out-of-range slot, position or page id,
+ *    a compress request with fewer than 2 pages) never fault: the offending
+ *    item is skipped and a bit is set in the device error word (gp_err_bits),
+ *    read with gp_get_device_errors.  A failed HIP launch returns GP_ERR_HIP.
+ *  - Threads: one context per host thread.
+ *  - Data types: fp32 for queries and query states, bf16 (raw uint16 bits)
+ *    for keys and values, int32 for ids and counts.
+ *
+ * Layouts (row-major, outermost first)
+ *  - K and V pools: [L][num_pages][Hkv][b][d] bf16.  A page id is shared by
+ *    all layers; logical slot i of a request lives in page
+ *    block_table[i / b] at offset i % b.
+ *  - Query-state pool (Appendix E.1 Eq. 11): [L][M][2][Hq][d] fp32, index 0
+ *    of the third axis is the short-timescale summary, 1 the long one.
+ *  - Queries: [B][L][Hq][d] fp32, the normalised query before RoPE (§3.2).
+ *  - Rotary table: [rope_rows][d] fp32; row p holds cos(p * f_j) for the d/2
+ *    frequencies f_j, then sin(p * f_j) (rotate-half pairing (j, j + d/2)).
+ *
+ * Version 1 limits: d = 128, b = 256, Hq / Hkv = 4, batch <= 1024.
+ */
+#ifndef GROWPAGE_H
+#define GROWPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gp_status {
+  GP_OK = 0,
+  GP_ERR_INVALID_ARG = 1, /* a null pointer, bad shape or inconsistent size */
+  GP_ERR_UNSUPPORTED = 2, /* valid but outside the version 1 limits */
+  GP_ERR_WORKSPACE = 3,   /* workspace missing, too small or not from gp_demand */
+  GP_ERR_HIP = 4          /* a HIP runtime call failed (see gp_last_hip_error) */
+} gp_status;
+
+/* Device error bits, OR-ed into the context's device error word. */
+enum gp_err_bits {
+  GP_DEVERR_SLOT = 1,      /* slot outside [0, max_slots): item skipped */
+  GP_DEVERR_POSITION = 2,  /* position outside [0, rope_rows): clamped */
+  GP_DEVERR_PAGE = 4,      /* page id outside [0, num_pages): tile skipped */
+  GP_DEVERR_SHORT = 8,     /* compress requested with fewer than 2 pages */
+  GP_DEVERR_PAGES = 16     /* device page count outside [1, max_pages] */
+};
+
+/* Actions and decisions (int8 on the device). */
+#define GP_COMPRESS 0
+#define GP_GROW 1
+
+/* Method parameters; defaults in brackets are the pages'. */
+typedef struct gp_config {
+  int32_t num_layers;    /* L */
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv; query head q uses KV head q / (Hq / Hkv) */
+  int32_t head_dim;      /* d [128] */
+  int32_t page_size;     /* b, tokens per page [256] (§5.1) */
+  int32_t recent_window; /* |R_t|, newest tokens never evicted [16] (§3.3) */
+  int32_t local_quota;   /* k_loc, per-block minimum retention [64] (App. D.2); 0 = plain top-k */
+  int32_t p_num, p_den;  /* coverage p = p_num / p_den [99/100] (§3.2 Eq. 7) */
+  double tau;            /* demand threshold [0] (§3.2, App. D.1) */
+  float alpha_short;     /* new-query weight 1 - beta_S [0.1] (§3.2 Eq. 6) */
+  float alpha_long;      /* new-query weight 1 - beta_L [0.001] */
+  int32_t max_slots;     /* M, query-state slots [512] (App. E.1) */
+} gp_config;
+
+/* Global page pool (§4.2): K/V storage and the device free-page stack. */
+typedef struct gp_pool {
+  uint16_t* k_pool;     /* device bf16 [L][num_pages][Hkv][b][d] */
+  uint16_t* v_pool;     /* device bf16, same layout */
+  int32_t num_pages;    /* pages in the pool */
+  int32_t* free_stack;  /* device int32 [num_pages]; free ids in [0, free_count) */
+  int32_t* free_count;  /* device int32 [1]; top of stack is free_stack[free_count - 1] */
+} gp_pool;
+
+/* A batch of requests at their capacity boundary (N = P * b for each). */
+typedef struct gp_batch {
+  int32_t batch;                 /* B */
+  int32_t max_pages;             /* row stride of block_table */
+  int32_t* block_table;          /* device int32 [B][max_pages] page ids */
+  int32_t* num_pages;            /* device int32 [B] P (gp_grow_page increments) */
+  int32_t* num_tokens;           /* device int32 [B] N (gp_compress_hold writes (P-1) b) */
+  const int32_t* slot;           /* device int32 [B] query-state slot */
+  const int32_t* position;       /* device int32 [B] absolute position of the current query */
+  const int32_t* num_pages_host; /* host int32 [B], equal to num_pages at the call */
+} gp_batch;
+
+/* Outputs of gp_demand (device). */
+typedef struct gp_demand_out {
+  int32_t* k_short;  /* [B][L][Hkv] K^S = D_p of the short view over C_t (Eq. 7) */
+  int32_t* k_long;   /* [B][L][Hkv] K^L */
+  int64_t* k_diff;   /* [B] sum K^S - sum K^L (may be NULL) */
+  double* delta;     /* [B] Delta_t = r^S - r^L (Eq. 8) (may be NULL) */
+  int8_t* decision;  /* [B] GP_GROW iff Delta_t > tau, else GP_COMPRESS */
+  float* abar;       /* optional [sum over rows of N][2]: the full-cache attention
+                        distributions (short, long) per token, rows in (request,
+                        layer, KV head) order; NULL skips the write */
+} gp_demand_out;
+
+typedef struct gp_counters {
+  int64_t grown;     /* pages granted by gp_grow_page */
+  int64_t compress;  /* Compress & Hold actions (decisions plus fallbacks) */
+  int64_t fallback;  /* Grow decisions that fell back (§4.2, App. H.2) */
+} gp_counters;
+
+typedef struct gp_ctx gp_ctx;
+
+/* Creates a context on the current HIP device.  Validates the config:
+ * Hq % Hkv == 0, 0 <= recent_window < page_size, local_quota >= 0,
+ * 0 < p_num <= p_den <= 2^20, 0 < alpha <= 1, max_slots >= 1. */
+gp_status gp_create(const gp_config* cfg, gp_ctx** out);
+void gp_destroy(gp_ctx* ctx);
+
+/* Workspace bytes gp_demand and gp_compress_hold need for `batch` requests
+ * holding `total_tokens` cached tokens in all (sum of N). */
+size_t gp_workspace_bytes(const gp_ctx* ctx, int32_t batch, int64_t total_tokens);
+
+/* A0: dual-timescale summaries (§3.2 Eq. 6; App. E.1 "Initialization and
+ * online update").  For each request b and summary x in {short, long}:
+ *   first_step[b] != 0:  qbar = q                   (slot (re)initialisation)
+ *   otherwise:           qbar = qbar + alpha_x (q - qbar)   (= beta qbar + (1-beta) q)
+ * qstate [L][M][2][Hq][d] is updated in place; q is [B][L][Hq][d];
+ * slot, first_step are device [B]. */
+gp_status gp_update_summaries(gp_ctx* ctx, float* qstate, const float* q,
+                              const int32_t* slot, const uint8_t* first_step,
+                              int32_t batch, void* stream);
+
+/* A1-A5: online demand estimation (§3.2; App. E.1 "Demand estimation at
+ * capacity boundaries").  Per request: calibrate each summary to the RMS of
+ * the current query q_cur (Eq. 12), rotate it to the current position, score
+ * it against every cached key of every (layer, KV head), form the attention
+ * distributions over the historical candidates C_t (all slots but the newest
+ * page) and over all slots, compute K^S, K^L (Eq. 7), Delta (Eq. 8) and the
+ * decision.  Requires N = P * b; P comes from num_pages_host (checked against
+ * the device copy).  A request with P = 1 has no candidates and is given
+ * GP_GROW with Delta = 0.  The workspace keeps the per-token importance the
+ * next gp_compress_hold on the same batch uses.
+ * qstate [L][M][2][Hq][d]; q_cur [B][L][Hq][d]; rope [rope_rows][d]. */
+gp_status gp_demand(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
+                    const float* qstate, const float* q_cur, const float* rope,
+                    int32_t rope_rows, void* workspace, size_t workspace_bytes,
+                    const gp_demand_out* out, void* stream);
+
+/* A6: Grow by One Page with fallback (§3.3; §4.2; App. H.2).  Requests are
+ * served in index order: a request whose decision is GP_GROW takes the page on
+ * top of the free stack while more than reserve_pages are free and its block
+ * table has room; the page is appended to its block table and P += 1.
+ * Otherwise it falls back to compression.  action[b] receives GP_GROW or
+ * GP_COMPRESS; decision may come from gp_demand or from the caller (policy
+ * variants).  Page counts never decrease (§3.3). */
+gp_status gp_grow_page(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
+                       const int8_t* decision, int8_t* action,
+                       int32_t reserve_pages, void* stream);
+
+/* A7-A9: Compress & Hold (§3.3 Eq. 9-10; §4.2; App. E.2) for every request
+ * whose action is GP_COMPRESS (action == NULL: every request).  Per (layer,
+ * KV head): importance s_i = max of the two full-cache distributions (Eq. 9);
+ * the newest recent_window slots are kept; each logical page keeps its top
+ * local_quota candidates; the rest of the budget (P-1) b - recent_window goes
+ * to the globally most important remaining candidates (ties: newer slot
+ * first); exactly b candidates are dropped and the kept K/V rows move, in
+ * slot order, to slots 0 .. (P-1) b - 1 of the same pages.  num_tokens
+ * becomes (P-1) b; block tables and P are unchanged.  Must follow gp_demand
+ * on the same batch with the same workspace.  dropped_out (optional, device
+ * int32 [B][L][Hkv][b]) receives the dropped slots in ascending order; rows of
+ * requests that do not compress are left unwritten. */
+gp_status gp_compress_hold(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
+                           const int8_t* action, void* workspace,
+                           size_t workspace_bytes, int32_t* dropped_out,
+                           void* stream);
+
+/* Copies the device counters to *out (synchronises the device). */
+gp_status gp_get_counters(gp_ctx* ctx, gp_counters* out);
+
+/* Returns the device error word (gp_err_bits) in *bits and clears it
+ * (synchronises the device). */
+gp_status gp_get_device_errors(gp_ctx* ctx, int32_t* bits);
+
+const char* gp_status_str(gp_status status);
+
+/* The last HIP error code seen by the context (0 = none). */
+int gp_last_hip_error(const gp_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GROWPAGE_H */

@@ -1,0 +1,233 @@
+// C ABI of the GrowPage boundary-event library: validation, workspace
+// carving and launch sequencing.  Kernels live in the k_*.hip files.
+// Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
+// Reasoning Serving" (arXiv 2609.03494).
+#include <new>
+#include <vector>
+
+#include "gp_internal.h"
+
+struct gp_ctx {
+  gp::Params p;
+  int device = 0;
+  int64_t* d_counters = nullptr;  // [3]
+  int32_t* d_err = nullptr;       // [1], right after the counters
+  int last_hip = 0;
+  // bookkeeping of the last gp_demand, checked by gp_compress_hold
+  const void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int batch = 0;
+  int64_t total_tokens = 0;
+  std::vector<int32_t> pages;  // P per request at gp_demand time
+};
+
+namespace {
+
+gp_status hip_fail(gp_ctx* c, hipError_t e) {
+  if (e == hipSuccess) return GP_OK;
+  c->last_hip = (int)e;
+  return GP_ERR_HIP;
+}
+
+bool shape_supported(const gp::Params& p) {
+  return p.d == gp::kD && p.b == gp::kPage && p.Hq == gp::kGroup * p.Hkv;
+}
+
+gp_status check_batch(const gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
+                      int64_t* total_pages) {
+  if (!pool || !bt) return GP_ERR_INVALID_ARG;
+  if (!pool->k_pool || !pool->v_pool || pool->num_pages < 1) return GP_ERR_INVALID_ARG;
+  if (bt->batch < 1 || bt->max_pages < 1 || !bt->block_table || !bt->num_pages ||
+      !bt->num_tokens || !bt->slot || !bt->position || !bt->num_pages_host)
+    return GP_ERR_INVALID_ARG;
+  if (bt->batch > gp::kMaxBatch) return GP_ERR_UNSUPPORTED;
+  int64_t tot = 0;
+  for (int r = 0; r < bt->batch; ++r) {
+    const int32_t P = bt->num_pages_host[r];
+    if (P < 1 || P > bt->max_pages) return GP_ERR_INVALID_ARG;
+    tot += P;
+  }
+  (void)c;
+  *total_pages = tot;
+  return GP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
+  if (!cfg || !out) return GP_ERR_INVALID_ARG;
+  *out = nullptr;
+  gp::Params p{};
+  p.L = cfg->num_layers;
+  p.Hq = cfg->num_q_heads;
+  p.Hkv = cfg->num_kv_heads;
+  p.d = cfg->head_dim;
+  p.b = cfg->page_size;
+  p.R = cfg->recent_window;
+  p.kloc = cfg->local_quota;
+  p.p_num = cfg->p_num;
+  p.p_den = cfg->p_den;
+  p.tau = cfg->tau;
+  p.alpha_s = cfg->alpha_short;
+  p.alpha_l = cfg->alpha_long;
+  p.M = cfg->max_slots;
+  if (p.L < 1 || p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0 || p.d < 2 || p.d % 2 != 0 ||
+      p.b < 1 || p.R < 0 || p.R >= p.b || p.kloc < 0 || p.p_num <= 0 || p.p_den < p.p_num ||
+      p.p_den > (1 << 20) || !(p.alpha_s > 0.0f && p.alpha_s <= 1.0f) ||
+      !(p.alpha_l > 0.0f && p.alpha_l <= 1.0f) || p.M < 1 || p.tau != p.tau)
+    return GP_ERR_INVALID_ARG;
+  gp_ctx* c = new (std::nothrow) gp_ctx();
+  if (!c) return GP_ERR_INVALID_ARG;
+  c->p = p;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&c->d_counters), 64);
+  if (e == hipSuccess) e = hipMemset(c->d_counters, 0, 64);
+  if (e != hipSuccess) {
+    if (c->d_counters) (void)hipFree(c->d_counters);
+    delete c;
+    return GP_ERR_HIP;
+  }
+  c->d_err = reinterpret_cast<int32_t*>(c->d_counters + 3);
+  *out = c;
+  return GP_OK;
+}
+
+void gp_destroy(gp_ctx* c) {
+  if (!c) return;
+  if (c->d_counters) (void)hipFree(c->d_counters);
+  delete c;
+}
+
+size_t gp_workspace_bytes(const gp_ctx* c, int32_t batch, int64_t total_tokens) {
+  if (!c || batch < 1 || total_tokens < 0) return 0;
+  return gp::ws_layout(c->p, batch, total_tokens).total;
+}
+
+gp_status gp_update_summaries(gp_ctx* c, float* qstate, const float* q, const int32_t* slot,
+                              const uint8_t* first_step, int32_t batch, void* stream) {
+  if (!c || !qstate || !q || !slot || !first_step || batch < 1) return GP_ERR_INVALID_ARG;
+  if (c->p.d != gp::kD) return GP_ERR_UNSUPPORTED;
+  return hip_fail(c, gp::launch_ema(c->p, qstate, q, slot, first_step, batch, c->d_err,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const float* qstate,
+                    const float* q_cur, const float* rope, int32_t rope_rows, void* ws,
+                    size_t ws_bytes, const gp_demand_out* out, void* stream) {
+  if (!c || !qstate || !q_cur || !rope || rope_rows < 1 || !out || !out->k_short ||
+      !out->k_long || !out->decision)
+    return GP_ERR_INVALID_ARG;
+  if (!shape_supported(c->p)) return GP_ERR_UNSUPPORTED;
+  int64_t total_pages = 0;
+  gp_status st = check_batch(c, pool, bt, &total_pages);
+  if (st != GP_OK) return st;
+  const int B = bt->batch;
+  const int64_t total_tokens = total_pages * c->p.b;
+  const gp::WsLayout w = gp::ws_layout(c->p, B, total_tokens);
+  if (!ws || ws_bytes < w.total) return GP_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gp::launch_plan(c->p, bt->num_pages, B, bt->max_pages, total_pages, ws,
+                                 c->d_err, s);
+  if (e == hipSuccess)
+    e = gp::launch_qhat(c->p, qstate, q_cur, rope, rope_rows, bt->slot, bt->position, B, ws,
+                        c->d_err, s);
+  if (e == hipSuccess)
+    e = gp::launch_score(c->p, w, pool->k_pool, pool->num_pages, bt->block_table,
+                         bt->max_pages, B, ws, c->d_err, s);
+  if (e == hipSuccess)
+    e = gp::launch_rowstats(c->p, w, B, ws, out->k_short, out->k_long, out->abar, s);
+  if (e == hipSuccess)
+    e = gp::launch_decide(c->p, B, ws, out->k_short, out->k_long, out->k_diff, out->delta,
+                          out->decision, s);
+  if (e != hipSuccess) {
+    c->ws = nullptr;
+    return hip_fail(c, e);
+  }
+  c->ws = ws;
+  c->ws_bytes = ws_bytes;
+  c->batch = B;
+  c->total_tokens = total_tokens;
+  c->pages.assign(bt->num_pages_host, bt->num_pages_host + B);
+  return GP_OK;
+}
+
+gp_status gp_grow_page(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
+                       const int8_t* decision, int8_t* action, int32_t reserve_pages,
+                       void* stream) {
+  if (!c || !decision || !action || reserve_pages < 0) return GP_ERR_INVALID_ARG;
+  if (!pool || !pool->free_stack || !pool->free_count || pool->num_pages < 1)
+    return GP_ERR_INVALID_ARG;
+  if (!bt || bt->batch < 1 || !bt->block_table || !bt->num_pages || bt->max_pages < 1)
+    return GP_ERR_INVALID_ARG;
+  if (bt->batch > gp::kMaxBatch) return GP_ERR_UNSUPPORTED;
+  return hip_fail(c, gp::launch_grow(bt->batch, bt->max_pages, pool->num_pages,
+                                     bt->block_table, bt->num_pages, pool->free_stack,
+                                     pool->free_count, reserve_pages, decision, action,
+                                     c->d_counters, c->d_err, static_cast<hipStream_t>(stream)));
+}
+
+gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
+                           const int8_t* action, void* ws, size_t ws_bytes,
+                           int32_t* dropped_out, void* stream) {
+  if (!c || !pool || !bt || !pool->k_pool || !pool->v_pool || !bt->block_table ||
+      !bt->num_tokens)
+    return GP_ERR_INVALID_ARG;
+  if (!shape_supported(c->p)) return GP_ERR_UNSUPPORTED;
+  if (!ws || ws != c->ws || ws_bytes != c->ws_bytes || bt->batch != c->batch)
+    return GP_ERR_WORKSPACE;
+  const gp::Params& p = c->p;
+  // Eq. 10 needs the local quotas to fit the budget K_t = (P - 1) b - R.
+  for (int r = 0; r < c->batch; ++r) {
+    const int64_t P = c->pages[r];
+    if (P < 2) continue;  // flagged on the device if it is asked to compress
+    if (P * p.b > 65536) return GP_ERR_UNSUPPORTED;
+    const int64_t kq = p.kloc;
+    const int64_t loc = (P - 1) * (kq < p.b ? kq : p.b) + (kq < p.b - p.R ? kq : p.b - p.R);
+    if (loc > (P - 1) * p.b - p.R) return GP_ERR_UNSUPPORTED;
+  }
+  const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);
+  if (e == hipSuccess)
+    e = gp::launch_compact(p, w, c->batch, action, pool->k_pool, pool->v_pool, pool->num_pages,
+                           bt->block_table, bt->max_pages, bt->num_tokens, ws, c->d_counters,
+                           c->d_err, s);
+  return hip_fail(c, e);
+}
+
+gp_status gp_get_counters(gp_ctx* c, gp_counters* out) {
+  if (!c || !out) return GP_ERR_INVALID_ARG;
+  int64_t h[3];
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(h, c->d_counters, sizeof h, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  out->grown = h[0];
+  out->compress = h[1];
+  out->fallback = h[2];
+  return GP_OK;
+}
+
+gp_status gp_get_device_errors(gp_ctx* c, int32_t* bits) {
+  if (!c || !bits) return GP_ERR_INVALID_ARG;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(bits, c->d_err, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(c->d_err, 0, sizeof(int32_t));
+  return hip_fail(c, e);
+}
+
+const char* gp_status_str(gp_status st) {
+  switch (st) {
+    case GP_OK: return "ok";
+    case GP_ERR_INVALID_ARG: return "invalid argument";
+    case GP_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case GP_ERR_WORKSPACE: return "workspace missing, too small or not prepared by gp_demand";
+    case GP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int gp_last_hip_error(const gp_ctx* c) { return c ? c->last_hip : 0; }
+
+}  // extern "C"

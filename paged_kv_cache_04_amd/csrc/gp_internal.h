@@ -1,0 +1,131 @@
+// Internal definitions of the GrowPage boundary-event library (gfx950).
+// Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
+// Reasoning Serving" (arXiv 2609.03494).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/growpage.h"
+
+namespace gp {
+
+// Version-1 kernel shape: head_dim 128, page 256, 4 query heads per KV head,
+// so each row is scored by 2 views x 4 heads = 8 summary queries.
+constexpr int kD = 128;
+constexpr int kPage = 256;
+constexpr int kGroup = 4;
+constexpr int kNQ = 2 * kGroup;
+constexpr int kMaxBatch = 1024;
+constexpr uint64_t kWsMagic = 0x4750574b53503031ull;  // "GPWKSP01"
+
+// Fixed-point scale for exact, order-free sums of probabilities: values in
+// [0, 1] are floored to multiples of 2^-40 and summed as uint64.
+constexpr float kFix = 1099511627776.0f;       // 2^40
+constexpr float kFixInv = 9.094947017729282e-13f;  // 2^-40
+
+struct Params {
+  int L, Hq, Hkv, d, b, R, kloc, p_num, p_den, M;
+  double tau;
+  float alpha_s, alpha_l;
+};
+
+// Workspace layout, identical for gp_demand and gp_compress_hold.
+struct WsHeader {
+  uint64_t magic;
+  int32_t batch;
+  int32_t valid;         // 1 once the plan kernel accepted the batch
+  int64_t total_tokens;  // sum of N over the batch
+  int64_t pad[5];
+};
+
+struct WsLayout {
+  size_t header, page_off, qhat, logits, pmax, imp, keys, dropped, total;
+  int64_t rows, row_tokens, row_pages;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(const Params& p, int B, int64_t total_tokens) {
+  WsLayout w{};
+  const int64_t lh = (int64_t)p.L * p.Hkv;
+  w.rows = (int64_t)B * lh;
+  w.row_tokens = lh * total_tokens;
+  w.row_pages = lh * (total_tokens / p.b);
+  size_t o = 0;
+  w.header = o;   o = align256(o + sizeof(WsHeader));
+  w.page_off = o; o = align256(o + sizeof(int64_t) * (B + 1));
+  w.qhat = o;     o = align256(o + sizeof(float) * (size_t)w.rows * kNQ * kD);
+  w.logits = o;   o = align256(o + sizeof(float) * (size_t)w.row_tokens * kNQ);
+  w.pmax = o;     o = align256(o + sizeof(float) * (size_t)w.row_pages * kNQ);
+  w.imp = o;      o = align256(o + sizeof(float) * (size_t)w.row_tokens);
+  w.keys = o;     o = align256(o + sizeof(float) * (size_t)w.row_tokens * 2);
+  w.dropped = o;  o = align256(o + sizeof(int32_t) * (size_t)w.rows * p.b);
+  w.total = o;
+  return w;
+}
+
+// ---- device arithmetic -----------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// exp(x) for x <= 0: Cody & Waite reduction x = n ln2 + r (ln2 as a 16-bit
+// head 0x1.62e4p-1 plus an fp32 tail), degree-6 Taylor polynomial of e^r in
+// Horner form, scale by 2^n built in the exponent field; zero once n < -100
+// so all later values stay normal fp32 numbers.
+__device__ __forceinline__ float gp_exp(float x) {
+  const float n = __builtin_rintf(x * 0x1.715476p+0f);
+  if (n < -100.0f) return 0.0f;
+  float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
+  r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+  float p = 1.0f / 720.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return p * __uint_as_float((uint32_t)(127 + (int)n) << 23);
+}
+
+// Mass of a probability in 2^-40 units (exact: v * 2^40 <= 2^40).
+__device__ __forceinline__ uint64_t fix40(float v) { return (uint64_t)(v * kFix); }
+
+// ---- launchers (each returns the hipError_t of its launch) -----------------
+
+hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int32_t* slot,
+                      const uint8_t* first, int B, int32_t* err, hipStream_t s);
+
+hipError_t launch_plan(const Params& p, const int32_t* num_pages_dev, int B, int max_pages,
+                       int64_t host_total_pages, void* ws, int32_t* err, hipStream_t s);
+
+hipError_t launch_qhat(const Params& p, const float* qstate, const float* qcur,
+                       const float* rope, int rope_rows, const int32_t* slot,
+                       const int32_t* position, int B, void* ws, int32_t* err, hipStream_t s);
+
+hipError_t launch_score(const Params& p, const WsLayout& w, const uint16_t* k_pool,
+                        int pool_pages, const int32_t* block_table, int max_pages, int B,
+                        void* ws, int32_t* err, hipStream_t s);
+
+hipError_t launch_rowstats(const Params& p, const WsLayout& w, int B, void* ws,
+                           int32_t* k_short, int32_t* k_long, float* abar, hipStream_t s);
+
+hipError_t launch_decide(const Params& p, int B, const void* ws, const int32_t* k_short,
+                         const int32_t* k_long, int64_t* k_diff, double* delta,
+                         int8_t* decision, hipStream_t s);
+
+hipError_t launch_grow(int B, int max_pages, int pool_pages, int32_t* block_table,
+                       int32_t* num_pages, const int32_t* free_stack, int32_t* free_count, int reserve,
+                       const int8_t* decision, int8_t* action, int64_t* counters,
+                       int32_t* err, hipStream_t s);
+
+hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t* action,
+                         void* ws, int32_t* dropped_out, int32_t* err, hipStream_t s);
+
+hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
+                          uint16_t* k_pool, uint16_t* v_pool, int pool_pages,
+                          const int32_t* block_table, int max_pages, int32_t* num_tokens,
+                          const void* ws, int64_t* counters, int32_t* err, hipStream_t s);
+
+}  // namespace gp

@@ -1,0 +1,112 @@
+// A9: in-place compaction of one row's K or V chain (§3.3 "compacted within
+// the existing physical-page allocation"; §4.2; App. E.2: at most (P - 1) b
+// occupied slots).  Citations are to "GrowPage: On-Demand KV Budgeting for
+// Efficient LLM Reasoning Serving" (arXiv 2609.03494).
+//
+// Kept slots keep their order and move to destination j = slot - #(dropped
+// before slot); for destination j the source is j + #{k : d_k - k <= j},
+// found by binary search over the 256 sorted dropped slots d_k.  Slots before
+// the first dropped one stay where they are.  Each source lies at most b
+// slots after its destination, so the workgroup walks destinations in
+// 256-row chunks: it loads a whole chunk into registers, waits for the loads
+// and barriers, then stores.  A chunk's stores land below every later
+// chunk's sources, and every earlier chunk has finished reading, so the
+// in-place move needs no copy of the row.  K and V rows, and different rows,
+// are disjoint and run as separate workgroups.
+#include "gp_internal.h"
+
+namespace gp {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCT = 256;                      // threads; one per dropped slot
+constexpr int kMaxPages = 65536 / kPage;      // pages per row held in LDS
+
+__global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool_pages,
+                                                 const WsHeader* __restrict__ hdr,
+                                                 const int64_t* __restrict__ page_off,
+                                                 const int8_t* __restrict__ action,
+                                                 uint16_t* __restrict__ k_pool,
+                                                 uint16_t* __restrict__ v_pool,
+                                                 const int32_t* __restrict__ block_table,
+                                                 int max_pages, int32_t* __restrict__ num_tokens,
+                                                 const int32_t* __restrict__ dropped,
+                                                 int32_t* __restrict__ err) {
+  __shared__ int32_t gap[kPage];
+  __shared__ int32_t pg[kMaxPages];
+  __shared__ int bad;
+  if (!hdr->valid) return;
+  const int LH = L * Hkv;
+  const int row = blockIdx.x >> 1, which = blockIdx.x & 1;
+  const int r = row / LH, lh = row % LH;
+  if (action && action[r] != GP_COMPRESS) return;
+  const int64_t P = page_off[r + 1] - page_off[r];
+  if (P < 2) return;
+  const int l = lh / Hkv, h = lh % Hkv;
+  const int t = threadIdx.x;
+  if (t == 0) bad = 0;
+  __syncthreads();
+  gap[t] = dropped[(int64_t)row * b + t] - t;
+  for (int i = t; i < P; i += kCT) {
+    const int page = block_table[(int64_t)r * max_pages + i];
+    if (page < 0 || page >= pool_pages) bad = 1;
+    pg[i] = page;
+  }
+  __syncthreads();
+  if (bad) {
+    if (t == 0) atomicOr(err, GP_DEVERR_PAGE);
+    return;
+  }
+  uint16_t* pool = which ? v_pool : k_pool;
+  // element offset of slot i of this row
+  auto slot_base = [&](int i) -> int64_t {
+    return (((int64_t)l * pool_pages + pg[i >> 8]) * Hkv + h) * (int64_t)(kPage * kD) +
+           (int64_t)(i & (kPage - 1)) * kD;
+  };
+  const int end = (int)((P - 1) * b);
+  const int d0 = gap[0] > 0 ? gap[0] : 0;
+  for (int c0 = d0; c0 < end; c0 += kCT) {
+    u32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int piece = u * kCT + t;
+      const int drow = c0 + (piece >> 4), part = piece & 15;
+      if (drow < end) {
+        int lo = 0, hi = kPage;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (gap[mid] <= drow) lo = mid + 1; else hi = mid;
+        }
+        const int src = drow + lo;
+        v[u] = *reinterpret_cast<const u32x4*>(pool + slot_base(src) + part * 8);
+      }
+    }
+    // every source of this chunk must be read before any of its stores
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int piece = u * kCT + t;
+      const int drow = c0 + (piece >> 4), part = piece & 15;
+      if (drow < end) *reinterpret_cast<u32x4*>(pool + slot_base(drow) + part * 8) = v[u];
+    }
+  }
+  if (lh == 0 && which == 0 && t == 0) num_tokens[r] = end;
+}
+
+hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
+                          uint16_t* k_pool, uint16_t* v_pool, int pool_pages,
+                          const int32_t* block_table, int max_pages, int32_t* num_tokens,
+                          const void* ws, int64_t* counters, int32_t* err, hipStream_t s) {
+  const char* base = static_cast<const char*>(ws);
+  hipLaunchKernelGGL(k_compact, dim3((unsigned)(w.rows * 2)), dim3(kCT), 0, s, p.L, p.Hkv, p.b,
+                     pool_pages, reinterpret_cast<const WsHeader*>(base + w.header),
+                     reinterpret_cast<const int64_t*>(base + w.page_off), action, k_pool, v_pool,
+                     block_table, max_pages, num_tokens,
+                     reinterpret_cast<const int32_t*>(base + w.dropped), err);
+  (void)B;
+  (void)counters;
+  return hipGetLastError();
+}
+
+}  // namespace gp

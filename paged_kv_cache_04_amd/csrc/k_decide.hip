@@ -1,0 +1,144 @@
+// A5: request-level trend and decision; A6: Grow by One Page with fallback.
+// Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
+// Reasoning Serving" (arXiv 2609.03494).
+#include "gp_internal.h"
+
+namespace gp {
+
+// ---------------------------------------------------------------------------
+// A5 (§3.2 Eq. 8 and the threshold rule).  r^x is the mean over the L*Hkv
+// (layer, KV head) pairs of K^x / |C_t|, so Delta = (sum K^S - sum K^L) /
+// (L * Hkv * |C_t|), evaluated in fp64 from the exact integer difference.
+// Grow iff Delta > tau.  A request of one page has no candidates: Delta = 0
+// and it grows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau,
+                                                const WsHeader* __restrict__ hdr,
+                                                const int64_t* __restrict__ page_off,
+                                                const int32_t* __restrict__ k_short,
+                                                const int32_t* __restrict__ k_long,
+                                                int64_t* __restrict__ k_diff,
+                                                double* __restrict__ delta,
+                                                int8_t* __restrict__ decision) {
+  __shared__ int64_t red[4];
+  if (!hdr->valid) return;
+  const int r = blockIdx.x, t = threadIdx.x;
+  int64_t s = 0;
+  for (int i = t; i < LH; i += 256)
+    s += (int64_t)k_short[(int64_t)r * LH + i] - (int64_t)k_long[(int64_t)r * LH + i];
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)(uint64_t)s, m);
+    const unsigned hi = __shfl_xor((unsigned)((uint64_t)s >> 32), m);
+    s += (int64_t)(((uint64_t)hi << 32) | lo);
+  }
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  if (t == 0) {
+    const int64_t diff = red[0] + red[1] + red[2] + red[3];
+    const int64_t P = page_off[r + 1] - page_off[r];
+    const int64_t card = (P - 1) * b;
+    double dl = 0.0;
+    int grow = 1;
+    if (card > 0) {
+      dl = (double)diff / ((double)LH * (double)card);
+      grow = dl > tau;
+    }
+    if (k_diff) k_diff[r] = diff;
+    if (delta) delta[r] = dl;
+    decision[r] = grow ? GP_GROW : GP_COMPRESS;
+  }
+}
+
+hipError_t launch_decide(const Params& p, int B, const void* ws, const int32_t* k_short,
+                         const int32_t* k_long, int64_t* k_diff, double* delta,
+                         int8_t* decision, hipStream_t s) {
+  const WsLayout w = ws_layout(p, B, 0);
+  const char* base = static_cast<const char*>(ws);
+  hipLaunchKernelGGL(k_decide, dim3(B), dim3(256), 0, s, p.L * p.Hkv, p.b, p.tau,
+                     reinterpret_cast<const WsHeader*>(base + w.header),
+                     reinterpret_cast<const int64_t*>(base + w.page_off), k_short, k_long,
+                     k_diff, delta, decision);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// A6 (§3.3 "Grow by One Page"; §4.2; App. H.2 defines a fallback).  Requests
+// are served in index order: the k-th request (0-based, counting only those
+// that want a page and have block-table room) is granted iff
+// k < free_count - reserve, and takes free_stack[free_count - 1 - k], i.e.
+// pages leave the top of the stack in request order.  That is the serial
+// rule computed with one block-wide prefix count.  Everyone else, including
+// growing requests that were refused, is marked for compression.
+// counters: [0] pages granted, [1] compress actions, [2] fallbacks.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int pool_pages,
+                                                    int32_t* __restrict__ block_table,
+                                                    int32_t* __restrict__ num_pages,
+                                                    const int32_t* __restrict__ free_stack,
+                                                    int32_t* __restrict__ free_count,
+                                                    int reserve,
+                                                    const int8_t* __restrict__ decision,
+                                                    int8_t* __restrict__ action,
+                                                    int64_t* __restrict__ counters,
+                                                    int32_t* __restrict__ err) {
+  __shared__ int scan[kMaxBatch];
+  __shared__ int n_fallback;
+  const int t = threadIdx.x;
+  if (t == 0) n_fallback = 0;
+  int fc = *free_count;
+  if (fc < 0 || fc > pool_pages) {
+    if (t == 0) atomicOr(err, GP_DEVERR_PAGES);
+    fc = 0;
+  }
+  const int avail = fc - reserve > 0 ? fc - reserve : 0;
+  bool dec_grow = false, want = false;
+  int P = 0;
+  if (t < B) {
+    dec_grow = decision[t] == GP_GROW;
+    P = num_pages[t];
+    want = dec_grow && P >= 1 && P < max_pages;
+  }
+  scan[t] = want ? 1 : 0;
+  __syncthreads();
+  for (int off = 1; off < kMaxBatch; off <<= 1) {
+    const int add = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  const int rank = scan[t] - (want ? 1 : 0);  // exclusive
+  const int total_want = scan[kMaxBatch - 1];
+  const bool granted = want && rank < avail;
+  if (t < B) {
+    if (granted) {
+      const int page = free_stack[fc - 1 - rank];
+      block_table[(int64_t)t * max_pages + P] = page;
+      num_pages[t] = P + 1;
+      action[t] = GP_GROW;
+    } else {
+      action[t] = GP_COMPRESS;
+      if (dec_grow) atomicAdd(&n_fallback, 1);
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    const int n_grant = total_want < avail ? total_want : avail;
+    *free_count = fc - n_grant;
+    counters[0] += n_grant;
+    counters[1] += B - n_grant;
+    counters[2] += n_fallback;
+  }
+}
+
+hipError_t launch_grow(int B, int max_pages, int pool_pages, int32_t* block_table,
+                       int32_t* num_pages, const int32_t* free_stack, int32_t* free_count,
+                       int reserve, const int8_t* decision, int8_t* action, int64_t* counters,
+                       int32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(k_grow, dim3(1), dim3(kMaxBatch), 0, s, B, max_pages, pool_pages,
+                     block_table, num_pages, free_stack, free_count, reserve, decision, action,
+                     counters, err);
+  return hipGetLastError();
+}
+
+}  // namespace gp

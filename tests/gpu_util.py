@@ -1,0 +1,119 @@
+"""Helpers shared by the GPU parity tests: wiring a synthetic workload into
+the binding, and running the oracle on host copies of the same inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import OracleConfig
+from paged_kv_cache_04_amd import binding as gb
+from paged_kv_cache_04_amd.runner import BoundaryRunner
+
+
+def log(msg: str):
+    print(msg, flush=True)
+
+
+def gb_config(shape, **kw) -> gb.Config:
+    return gb.Config(num_layers=shape.L, num_q_heads=shape.Hq, num_kv_heads=shape.Hkv,
+                     head_dim=shape.d, page_size=shape.b, **kw)
+
+
+def oracle_config(cfg: gb.Config) -> OracleConfig:
+    return OracleConfig(L=cfg.num_layers, Hq=cfg.num_q_heads, Hkv=cfg.num_kv_heads,
+                        d=cfg.head_dim, b=cfg.page_size, R=cfg.recent_window,
+                        k_loc=cfg.local_quota, p_num=cfg.p_num, p_den=cfg.p_den, tau=cfg.tau,
+                        alpha_s=cfg.alpha_short, alpha_l=cfg.alpha_long, M=cfg.max_slots)
+
+
+def bf16_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def runner_for(wl, cfg: gb.Config, want_abar=True, want_dropped=True) -> BoundaryRunner:
+    s = wl.shape
+    qstate = torch.zeros((s.L, wl.max_slots, 2, s.Hq, s.d), dtype=torch.float32, device=wl.device)
+    pool = gb.Pool(wl.k_pool, wl.v_pool, wl.free_stack, wl.free_count)
+    batch = gb.Batch(wl.block_table, wl.num_pages, wl.num_tokens, wl.slot, wl.position,
+                     wl.num_pages.cpu().numpy().astype(np.int32).copy())
+    return BoundaryRunner(cfg, pool, batch, qstate, wl.rope, want_abar=want_abar,
+                          want_dropped=want_dropped)
+
+
+def run_stream_gpu(run: BoundaryRunner, wl, steps=None):
+    steps = wl.steps if steps is None else steps
+    q = None
+    for t in range(steps):
+        q = wl.query(t)
+        run.update(q, wl.first_step(t))
+    return q
+
+
+def run_stream_oracle(wl, ocfg: OracleConfig, state=None, steps=None):
+    steps = wl.steps if steps is None else steps
+    if state is None:
+        state = np.zeros((ocfg.L, wl.max_slots, 2, ocfg.Hq, ocfg.d), dtype=np.float32)
+    slot = wl.slot.cpu().numpy()
+    q = None
+    for t in range(steps):
+        q = wl.query(t).cpu().numpy()
+        oracle.ema(ocfg, state, q, slot, wl.first_step(t).cpu().numpy())
+    return state, q
+
+
+class HostCopy:
+    """Host copies of the inputs the oracle needs."""
+
+    def __init__(self, wl):
+        self.k = bf16_np(wl.k_pool)
+        self.v = bf16_np(wl.v_pool)
+        self.bt = wl.block_table.cpu().numpy().copy()
+        self.P = wl.num_pages.cpu().numpy().astype(np.int32).copy()
+        self.free_stack = wl.free_stack.cpu().numpy().copy()
+        self.free_count = int(wl.free_count.item())
+        self.rope = wl.rope.cpu().numpy()
+        self.pos = wl.position.cpu().numpy()
+        self.slot = wl.slot.cpu().numpy()
+
+
+def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
+    """A1-A9 on host copies; returns a dict of every output."""
+    dem = oracle.demand(ocfg, lambda r, l, h, pages: oracle.gather_row(hc.k, l, h, pages),
+                        hc.bt, hc.P, state, qcur, hc.rope, hc.pos, hc.slot, want_abar=True)
+    bt = hc.bt.copy()
+    P = hc.P.copy()
+    action, fc, counters = oracle.grow(dem["decision"], bt, P, hc.free_stack, hc.free_count,
+                                       reserve)
+    B = len(P)
+    dropped = {}
+    compacted = {}
+    for r in range(B):
+        if action[r] != oracle.COMPRESS:
+            continue
+        pages = hc.bt[r, :hc.P[r]]
+        for l in range(ocfg.L):
+            for h in range(ocfg.Hkv):
+                keep = oracle.select(ocfg, dem["abar"][(r, l, h)])
+                N = keep.size
+                dropped[(r, l, h)] = np.nonzero(keep[:N - ocfg.R] == 0)[0].astype(np.int32)
+                ks = oracle.gather_row(hc.k, l, h, pages)
+                vs = oracle.gather_row(hc.v, l, h, pages)
+                n = oracle.compact(ks, keep)
+                oracle.compact(vs, keep)
+                compacted[(r, l, h)] = (ks[:n], vs[:n])
+    return dict(dem=dem, action=action, bt=bt, P=P, free_count=fc, counters=counters,
+                dropped=dropped, compacted=compacted)
+
+
+def row_offsets(P: np.ndarray, L: int, Hkv: int, b: int):
+    """Start of each (request, layer, KV head) row in the token-major outputs."""
+    offs = {}
+    o = 0
+    for r in range(len(P)):
+        N = int(P[r]) * b
+        for l in range(L):
+            for h in range(Hkv):
+                offs[(r, l, h)] = (o, N)
+                o += N
+    return offs
