@@ -17,7 +17,7 @@
  *  - Asynchrony: every gp_* call that takes a stream enqueues kernels on it
  *    and returns after host-side validation; results are valid once the
  *    stream has reached that point.  No call synchronises the device except
- *    gp_get_counters and gp_get_device_errors.
+ *    gp_get_counters, gp_get_device_errors and gp_profile_read.
  *  - Errors: host-checkable problems return an error status and enqueue
  *    nothing.  Device-side checks (out-of-range slot, position or page id,
  *    a compress request with fewer than 2 pages) never fault: the offending
@@ -190,6 +190,33 @@ gp_status gp_compress_hold(gp_ctx* ctx, const gp_pool* pool, const gp_batch* bat
                            const int8_t* action, void* workspace,
                            size_t workspace_bytes, int32_t* dropped_out,
                            void* stream);
+
+/* Kernels of the event, for gp_profile_read. */
+enum gp_kernel_id {
+  GP_K_EMA = 0,     /* A0 summary update */
+  GP_K_PLAN = 1,    /* batch prefix sums and validation */
+  GP_K_QHAT = 2,    /* A1 calibrate + rotate */
+  GP_K_SCORE = 3,   /* A2 paged key scoring */
+  GP_K_ROWSTATS = 4,/* A3-A4 distributions, importance, D_p */
+  GP_K_DECIDE = 5,  /* A5 trend and decision */
+  GP_K_GROW = 6,    /* A6 page grant and fallback */
+  GP_K_SELECT = 7,  /* A7-A8 window mask and Eq. 10 selection */
+  GP_K_COMPACT = 8, /* A9 in-place compaction */
+  GP_NUM_KERNELS = 9
+};
+
+typedef struct gp_kernel_times {
+  double ms[GP_NUM_KERNELS];        /* accumulated device time per kernel */
+  int64_t launches[GP_NUM_KERNELS]; /* launches recorded per kernel */
+} gp_kernel_times;
+
+/* Kernel timing for measurement.  enable != 0 clears the accumulators and
+ * from then on records a HIP event before and after every kernel the
+ * context launches, on the launch stream; enable == 0 stops recording.
+ * gp_profile_read synchronises on the recorded events, adds their elapsed
+ * times to the accumulators and copies them to *out. */
+gp_status gp_profile(gp_ctx* ctx, int enable);
+gp_status gp_profile_read(gp_ctx* ctx, gp_kernel_times* out);
 
 /* Copies the device counters to *out (synchronises the device). */
 gp_status gp_get_counters(gp_ctx* ctx, gp_counters* out);

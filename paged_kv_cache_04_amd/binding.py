@@ -22,8 +22,10 @@ GP_GROW = 1
 SYMBOLS = (
     "gp_create", "gp_destroy", "gp_workspace_bytes", "gp_update_summaries", "gp_demand",
     "gp_grow_page", "gp_compress_hold", "gp_get_counters", "gp_get_device_errors",
-    "gp_status_str", "gp_last_hip_error",
+    "gp_status_str", "gp_last_hip_error", "gp_profile", "gp_profile_read",
 )
+
+KERNELS = ("ema", "plan", "qhat", "score", "rowstats", "decide", "grow", "select", "compact")
 
 
 class GPError(RuntimeError):
@@ -62,6 +64,10 @@ class gp_demand_out(ctypes.Structure):
         ("k_short", ctypes.c_void_p), ("k_long", ctypes.c_void_p), ("k_diff", ctypes.c_void_p),
         ("delta", ctypes.c_void_p), ("decision", ctypes.c_void_p), ("abar", ctypes.c_void_p),
     ]
+
+
+class gp_kernel_times(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 9), ("launches", ctypes.c_int64 * 9)]
 
 
 class gp_counters(ctypes.Structure):
@@ -106,6 +112,10 @@ def load(path: str = LIB_PATH):
     L.gp_status_str.restype = ctypes.c_char_p
     L.gp_last_hip_error.argtypes = [vp]
     L.gp_last_hip_error.restype = ctypes.c_int
+    L.gp_profile.argtypes = [vp, ctypes.c_int]
+    L.gp_profile.restype = ctypes.c_int
+    L.gp_profile_read.argtypes = [vp, ctypes.POINTER(gp_kernel_times)]
+    L.gp_profile_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -277,3 +287,14 @@ def gp_get_device_errors(ctx: Context) -> int:
     v = ctypes.c_int32()
     _check(load().gp_get_device_errors(ctx.handle, ctypes.byref(v)), "gp_get_device_errors", ctx)
     return int(v.value)
+
+
+def gp_profile(ctx: Context, enable: bool):
+    _check(load().gp_profile(ctx.handle, 1 if enable else 0), "gp_profile", ctx)
+
+
+def gp_profile_read(ctx: Context) -> dict:
+    """{kernel name: (total ms, launches)} accumulated since gp_profile(ctx, True)."""
+    t = gp_kernel_times()
+    _check(load().gp_profile_read(ctx.handle, ctypes.byref(t)), "gp_profile_read", ctx)
+    return {k: (float(t.ms[i]), int(t.launches[i])) for i, k in enumerate(KERNELS)}

@@ -3,6 +3,7 @@
 // Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
 // Reasoning Serving" (arXiv 2609.03494).
 #include <new>
+#include <tuple>
 #include <vector>
 
 #include "gp_internal.h"
@@ -19,6 +20,12 @@ struct gp_ctx {
   int batch = 0;
   int64_t total_tokens = 0;
   std::vector<int32_t> pages;  // P per request at gp_demand time
+  // kernel timing (gp_profile)
+  bool profiling = false;
+  std::vector<hipEvent_t> free_events;
+  std::vector<std::tuple<int, hipEvent_t, hipEvent_t>> pending;
+  double ms[GP_NUM_KERNELS] = {};
+  int64_t launches[GP_NUM_KERNELS] = {};
 };
 
 namespace {
@@ -27,6 +34,30 @@ gp_status hip_fail(gp_ctx* c, hipError_t e) {
   if (e == hipSuccess) return GP_OK;
   c->last_hip = (int)e;
   return GP_ERR_HIP;
+}
+
+hipEvent_t take_event(gp_ctx* c) {
+  if (!c->free_events.empty()) {
+    hipEvent_t e = c->free_events.back();
+    c->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs one kernel launch; with profiling on, brackets it with events on s.
+template <class F>
+hipError_t timed(gp_ctx* c, int kid, hipStream_t s, F&& launch) {
+  if (!c->profiling) return launch();
+  hipEvent_t a = take_event(c), b = take_event(c);
+  if (!a || !b) return launch();
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  c->pending.emplace_back(kid, a, b);
+  return e;
 }
 
 bool shape_supported(const gp::Params& p) {
@@ -96,6 +127,11 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
 
 void gp_destroy(gp_ctx* c) {
   if (!c) return;
+  for (auto& t : c->pending) {
+    (void)hipEventDestroy(std::get<1>(t));
+    (void)hipEventDestroy(std::get<2>(t));
+  }
+  for (hipEvent_t e : c->free_events) (void)hipEventDestroy(e);
   if (c->d_counters) (void)hipFree(c->d_counters);
   delete c;
 }
@@ -109,8 +145,10 @@ gp_status gp_update_summaries(gp_ctx* c, float* qstate, const float* q, const in
                               const uint8_t* first_step, int32_t batch, void* stream) {
   if (!c || !qstate || !q || !slot || !first_step || batch < 1) return GP_ERR_INVALID_ARG;
   if (c->p.d != gp::kD) return GP_ERR_UNSUPPORTED;
-  return hip_fail(c, gp::launch_ema(c->p, qstate, q, slot, first_step, batch, c->d_err,
-                                    static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_fail(c, timed(c, GP_K_EMA, s, [&] {
+    return gp::launch_ema(c->p, qstate, q, slot, first_step, batch, c->d_err, s);
+  }));
 }
 
 gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const float* qstate,
@@ -128,19 +166,28 @@ gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const fl
   const gp::WsLayout w = gp::ws_layout(c->p, B, total_tokens);
   if (!ws || ws_bytes < w.total) return GP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gp::launch_plan(c->p, bt->num_pages, B, bt->max_pages, total_pages, ws,
-                                 c->d_err, s);
+  hipError_t e = timed(c, GP_K_PLAN, s, [&] {
+    return gp::launch_plan(c->p, bt->num_pages, B, bt->max_pages, total_pages, ws, c->d_err, s);
+  });
   if (e == hipSuccess)
-    e = gp::launch_qhat(c->p, qstate, q_cur, rope, rope_rows, bt->slot, bt->position, B, ws,
-                        c->d_err, s);
+    e = timed(c, GP_K_QHAT, s, [&] {
+      return gp::launch_qhat(c->p, qstate, q_cur, rope, rope_rows, bt->slot, bt->position, B,
+                             ws, c->d_err, s);
+    });
   if (e == hipSuccess)
-    e = gp::launch_score(c->p, w, pool->k_pool, pool->num_pages, bt->block_table,
-                         bt->max_pages, B, ws, c->d_err, s);
+    e = timed(c, GP_K_SCORE, s, [&] {
+      return gp::launch_score(c->p, w, pool->k_pool, pool->num_pages, bt->block_table,
+                              bt->max_pages, B, ws, c->d_err, s);
+    });
   if (e == hipSuccess)
-    e = gp::launch_rowstats(c->p, w, B, ws, out->k_short, out->k_long, out->abar, s);
+    e = timed(c, GP_K_ROWSTATS, s, [&] {
+      return gp::launch_rowstats(c->p, w, B, ws, out->k_short, out->k_long, out->abar, s);
+    });
   if (e == hipSuccess)
-    e = gp::launch_decide(c->p, B, ws, out->k_short, out->k_long, out->k_diff, out->delta,
-                          out->decision, s);
+    e = timed(c, GP_K_DECIDE, s, [&] {
+      return gp::launch_decide(c->p, B, ws, out->k_short, out->k_long, out->k_diff, out->delta,
+                               out->decision, s);
+    });
   if (e != hipSuccess) {
     c->ws = nullptr;
     return hip_fail(c, e);
@@ -162,10 +209,12 @@ gp_status gp_grow_page(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   if (!bt || bt->batch < 1 || !bt->block_table || !bt->num_pages || bt->max_pages < 1)
     return GP_ERR_INVALID_ARG;
   if (bt->batch > gp::kMaxBatch) return GP_ERR_UNSUPPORTED;
-  return hip_fail(c, gp::launch_grow(bt->batch, bt->max_pages, pool->num_pages,
-                                     bt->block_table, bt->num_pages, pool->free_stack,
-                                     pool->free_count, reserve_pages, decision, action,
-                                     c->d_counters, c->d_err, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_fail(c, timed(c, GP_K_GROW, s, [&] {
+    return gp::launch_grow(bt->batch, bt->max_pages, pool->num_pages, bt->block_table,
+                           bt->num_pages, pool->free_stack, pool->free_count, reserve_pages,
+                           decision, action, c->d_counters, c->d_err, s);
+  }));
 }
 
 gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
@@ -189,11 +238,56 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   }
   const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);
+  hipError_t e = timed(c, GP_K_SELECT, s, [&] {
+    return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);
+  });
   if (e == hipSuccess)
-    e = gp::launch_compact(p, w, c->batch, action, pool->k_pool, pool->v_pool, pool->num_pages,
-                           bt->block_table, bt->max_pages, bt->num_tokens, ws, c->d_counters,
-                           c->d_err, s);
+    e = timed(c, GP_K_COMPACT, s, [&] {
+      return gp::launch_compact(p, w, c->batch, action, pool->k_pool, pool->v_pool,
+                                pool->num_pages, bt->block_table, bt->max_pages, bt->num_tokens,
+                                ws, c->d_counters, c->d_err, s);
+    });
+  return hip_fail(c, e);
+}
+
+gp_status gp_profile(gp_ctx* c, int enable) {
+  if (!c) return GP_ERR_INVALID_ARG;
+  if (enable) {
+    for (auto& t : c->pending) {
+      c->free_events.push_back(std::get<1>(t));
+      c->free_events.push_back(std::get<2>(t));
+    }
+    c->pending.clear();
+    for (int k = 0; k < GP_NUM_KERNELS; ++k) {
+      c->ms[k] = 0.0;
+      c->launches[k] = 0;
+    }
+  }
+  c->profiling = enable != 0;
+  return GP_OK;
+}
+
+gp_status gp_profile_read(gp_ctx* c, gp_kernel_times* out) {
+  if (!c || !out) return GP_ERR_INVALID_ARG;
+  hipError_t e = hipSuccess;
+  for (auto& t : c->pending) {
+    const int kid = std::get<0>(t);
+    hipEvent_t a = std::get<1>(t), b = std::get<2>(t);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e == hipSuccess) {
+      c->ms[kid] += ms;
+      c->launches[kid] += 1;
+    }
+    c->free_events.push_back(a);
+    c->free_events.push_back(b);
+  }
+  c->pending.clear();
+  for (int k = 0; k < GP_NUM_KERNELS; ++k) {
+    out->ms[k] = c->ms[k];
+    out->launches[k] = c->launches[k];
+  }
   return hip_fail(c, e);
 }
 

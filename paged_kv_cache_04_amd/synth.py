@@ -199,17 +199,22 @@ def make_workload(shape: ModelShape, pages_per_request, pool_pages: int, *, seed
         u = (u_s if align[r] == "S" else u_l)[r]  # [L][Hkv][d]
         cos = rope[int(position[r]), :half]
         sin = rope[int(position[r]), half:]
-        cs = np.broadcast_to(np.asarray(cluster_sizes[r]), (s.L, s.Hkv))
         ndem = int(N[r]) - s.b
-        for l in range(s.L):
-            for h in range(s.Hkv):
-                c = int(min(cs[l, h], ndem))
-                slots = torch.from_numpy(rng.choice(ndem, size=c, replace=False).astype(np.int64)).to(device)
-                vec = cluster_scale * math.sqrt(s.d) * u[l, h][None, :] + 0.1 * torch.randn(
-                    (c, s.d), generator=g, device=device, dtype=torch.float32)
-                vec = rotate_keys(vec, cos, sin).to(torch.bfloat16)
-                pages = bt_t[r, slots // s.b].long()
-                k_pool[l, pages, h, slots % s.b] = vec
+        cs = np.minimum(np.broadcast_to(np.asarray(cluster_sizes[r]), (s.L, s.Hkv)), ndem)
+        cs = cs.astype(np.int64)
+        slots = np.concatenate([rng.choice(ndem, size=int(cs[l, h]), replace=False)
+                                for l in range(s.L) for h in range(s.Hkv)]).astype(np.int64)
+        li = np.repeat(np.arange(s.L), cs.sum(axis=1))
+        hi = np.concatenate([np.repeat(np.arange(s.Hkv), cs[l]) for l in range(s.L)])
+        S = torch.from_numpy(slots).to(device)
+        Lt = torch.from_numpy(li.astype(np.int64)).to(device)
+        Ht = torch.from_numpy(hi.astype(np.int64)).to(device)
+        vec = cluster_scale * math.sqrt(s.d) * u[Lt, Ht] + 0.1 * torch.randn(
+            (S.numel(), s.d), generator=g, device=device, dtype=torch.float32)
+        vec = rotate_keys(vec, cos, sin).to(torch.bfloat16)
+        pages = bt_t[r, S // s.b].long()
+        k_pool[Lt, pages, Ht, S % s.b] = vec
+        del vec
     i32 = dict(dtype=torch.int32, device=device)
     return Workload(
         shape=s, device=device, k_pool=k_pool, v_pool=v_pool, block_table=bt_t,
@@ -232,3 +237,37 @@ def tiny(variant: str, device="cpu") -> Workload:
     return make_workload(TINY, [4], 16, seed=SEED_BASE + 0, device=device, align=[align],
                          cluster_sizes=[8], cluster_scale=4.0, free_pages=free, max_pages=8,
                          steps=1024, short_steps=32, max_slots=8)
+
+
+def _log_uniform_sizes(rng, shape, lo=50, hi=4000):
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.int64)
+
+
+def llama8k(variant: str, device="cuda", pool_pages: int = 4096) -> Workload:
+    """Llama-8B shape (32 layers, 32 Q / 8 KV heads, d 128), one request of
+    8192 tokens = 32 pages scattered in a pool of pool_pages; per-row clusters
+    of log-uniform size in [50, 4000] on the long view ("grow") or the short
+    view ("compress")."""
+    seed = SEED_BASE + 1
+    rng = np.random.default_rng(seed + (0 if variant == "grow" else 17))
+    sizes = _log_uniform_sizes(rng, (LLAMA8B.L, LLAMA8B.Hkv))
+    return make_workload(LLAMA8B, [32], pool_pages, seed=seed, device=device,
+                         align=["L" if variant == "grow" else "S"], cluster_sizes=[sizes],
+                         free_pages=8, steps=256, short_steps=32)
+
+
+def batch64(device="cuda", pool_pages: int = 6144, seed: int = SEED_BASE + 3,
+            batch: int = 64, value_pool: bool = True) -> Workload:
+    """Continuous-serving snapshot: `batch` requests of Llama-8B shape with page
+    counts uniform in [4, 128] (1k-32k tokens), pages interleaved in one pool,
+    per request a cluster direction on the long (grow) or short (compress)
+    view with log-uniform per-row cluster sizes, and free pages for about a
+    third of the growing requests so that the rest fall back."""
+    rng = np.random.default_rng(seed)
+    P = rng.integers(4, 129, size=batch)
+    align = [str(a) for a in rng.choice(["S", "L"], size=batch)]
+    free = max(1, sum(a == "L" for a in align) // 3)
+    sizes = [_log_uniform_sizes(rng, (LLAMA8B.L, LLAMA8B.Hkv)) for _ in range(batch)]
+    return make_workload(LLAMA8B, P.tolist(), pool_pages, seed=seed, device=device, align=align,
+                         cluster_sizes=sizes, free_pages=free, max_pages=136, steps=256,
+                         short_steps=32, value_pool=value_pool)

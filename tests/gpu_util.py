@@ -63,23 +63,42 @@ def run_stream_oracle(wl, ocfg: OracleConfig, state=None, steps=None):
 
 
 class HostCopy:
-    """Host copies of the inputs the oracle needs."""
+    """Host copies of the inputs the oracle needs: only the pages the batch's
+    block tables reference are copied (pools of the full-size workloads are
+    far larger than host memory), with a map from pool page ids to them."""
 
     def __init__(self, wl):
-        self.k = bf16_np(wl.k_pool)
-        self.v = bf16_np(wl.v_pool)
         self.bt = wl.block_table.cpu().numpy().copy()
         self.P = wl.num_pages.cpu().numpy().astype(np.int32).copy()
+        used = np.unique(np.concatenate([self.bt[r, :self.P[r]] for r in range(len(self.P))]))
+        self.used = used
+        idx = torch.from_numpy(used.astype(np.int64)).to(wl.device)
+        self.k = bf16_np(wl.k_pool[:, idx])
+        self.v = bf16_np(wl.v_pool[:, idx])
+        self.remap = np.full(int(wl.k_pool.shape[1]), -1, dtype=np.int64)
+        self.remap[used] = np.arange(used.size)
         self.free_stack = wl.free_stack.cpu().numpy().copy()
         self.free_count = int(wl.free_count.item())
         self.rope = wl.rope.cpu().numpy()
         self.pos = wl.position.cpu().numpy()
         self.slot = wl.slot.cpu().numpy()
 
+    def keys(self, l, h, pages):
+        return oracle.gather_row(self.k, l, h, self.remap[np.asarray(pages)])
+
+    def values(self, l, h, pages):
+        return oracle.gather_row(self.v, l, h, self.remap[np.asarray(pages)])
+
+
+def device_rows(pool: torch.Tensor, l: int, h: int, pages) -> np.ndarray:
+    """One row chain gathered on the device, copied to the host as uint16."""
+    idx = torch.as_tensor(np.asarray(pages, dtype=np.int64), device=pool.device)
+    return bf16_np(pool[l, idx, h].reshape(-1, pool.shape[-1]))
+
 
 def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
     """A1-A9 on host copies; returns a dict of every output."""
-    dem = oracle.demand(ocfg, lambda r, l, h, pages: oracle.gather_row(hc.k, l, h, pages),
+    dem = oracle.demand(ocfg, lambda r, l, h, pages: hc.keys(l, h, pages),
                         hc.bt, hc.P, state, qcur, hc.rope, hc.pos, hc.slot, want_abar=True)
     bt = hc.bt.copy()
     P = hc.P.copy()
@@ -89,7 +108,7 @@ def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
     dropped = {}
     compacted = {}
     for r in range(B):
-        if action[r] != oracle.COMPRESS:
+        if action[r] != oracle.COMPRESS or hc.P[r] < 2:
             continue
         pages = hc.bt[r, :hc.P[r]]
         for l in range(ocfg.L):
@@ -97,8 +116,8 @@ def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
                 keep = oracle.select(ocfg, dem["abar"][(r, l, h)])
                 N = keep.size
                 dropped[(r, l, h)] = np.nonzero(keep[:N - ocfg.R] == 0)[0].astype(np.int32)
-                ks = oracle.gather_row(hc.k, l, h, pages)
-                vs = oracle.gather_row(hc.v, l, h, pages)
+                ks = hc.keys(l, h, pages)
+                vs = hc.values(l, h, pages)
                 n = oracle.compact(ks, keep)
                 oracle.compact(vs, keep)
                 compacted[(r, l, h)] = (ks[:n], vs[:n])
