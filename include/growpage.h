@@ -134,8 +134,10 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out);
 void gp_destroy(gp_ctx* ctx);
 
 /* Workspace bytes gp_demand and gp_compress_hold need for `batch` requests
- * holding `total_tokens` cached tokens in all (sum of N). */
-size_t gp_workspace_bytes(const gp_ctx* ctx, int32_t batch, int64_t total_tokens);
+ * holding `total_tokens` cached tokens in all (sum of N), the largest of them
+ * `max_tokens` (max of N).  Returns 0 on invalid arguments. */
+size_t gp_workspace_bytes(const gp_ctx* ctx, int32_t batch, int64_t total_tokens,
+                          int64_t max_tokens);
 
 /* A0: dual-timescale summaries (§3.2 Eq. 6; App. E.1 "Initialization and
  * online update").  For each request b and summary x in {short, long}:
@@ -194,15 +196,14 @@ gp_status gp_compress_hold(gp_ctx* ctx, const gp_pool* pool, const gp_batch* bat
 /* Kernels of the event, for gp_profile_read. */
 enum gp_kernel_id {
   GP_K_EMA = 0,     /* A0 summary update */
-  GP_K_PLAN = 1,    /* batch prefix sums and validation */
+  GP_K_PLAN = 1,    /* batch prefix sums, work order and validation */
   GP_K_QHAT = 2,    /* A1 calibrate + rotate */
-  GP_K_SCORE = 3,   /* A2 paged key scoring */
-  GP_K_ROWSTATS = 4,/* A3-A4 distributions, importance, D_p */
-  GP_K_DECIDE = 5,  /* A5 trend and decision */
-  GP_K_GROW = 6,    /* A6 page grant and fallback */
-  GP_K_SELECT = 7,  /* A7-A8 window mask and Eq. 10 selection */
-  GP_K_COMPACT = 8, /* A9 in-place compaction */
-  GP_NUM_KERNELS = 9
+  GP_K_DEMAND = 3,  /* A2-A4 paged key scoring, distributions, importance, D_p */
+  GP_K_DECIDE = 4,  /* A5 trend and decision */
+  GP_K_GROW = 5,    /* A6 page grant and fallback */
+  GP_K_SELECT = 6,  /* A7-A8 window mask and Eq. 10 selection */
+  GP_K_COMPACT = 7, /* A9 in-place compaction */
+  GP_NUM_KERNELS = 8
 };
 
 typedef struct gp_kernel_times {

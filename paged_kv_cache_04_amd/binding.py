@@ -25,7 +25,7 @@ SYMBOLS = (
     "gp_status_str", "gp_last_hip_error", "gp_profile", "gp_profile_read",
 )
 
-KERNELS = ("ema", "plan", "qhat", "score", "rowstats", "decide", "grow", "select", "compact")
+KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact")
 
 
 class GPError(RuntimeError):
@@ -67,7 +67,7 @@ class gp_demand_out(ctypes.Structure):
 
 
 class gp_kernel_times(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 9), ("launches", ctypes.c_int64 * 9)]
+    _fields_ = [("ms", ctypes.c_double * 8), ("launches", ctypes.c_int64 * 8)]
 
 
 class gp_counters(ctypes.Structure):
@@ -91,7 +91,7 @@ def load(path: str = LIB_PATH):
     L.gp_create.restype = ctypes.c_int
     L.gp_destroy.argtypes = [vp]
     L.gp_destroy.restype = None
-    L.gp_workspace_bytes.argtypes = [vp, i32, i64]
+    L.gp_workspace_bytes.argtypes = [vp, i32, i64, i64]
     L.gp_workspace_bytes.restype = sz
     L.gp_update_summaries.argtypes = [vp, vp, vp, vp, vp, i32, vp]
     L.gp_update_summaries.restype = ctypes.c_int
@@ -242,8 +242,8 @@ class DemandOut:
                              _ptr(self.delta), _ptr(self.decision), _ptr(self.abar))
 
 
-def gp_workspace_bytes(ctx: Context, batch: int, total_tokens: int) -> int:
-    return int(load().gp_workspace_bytes(ctx.handle, batch, total_tokens))
+def gp_workspace_bytes(ctx: Context, batch: int, total_tokens: int, max_tokens: int) -> int:
+    return int(load().gp_workspace_bytes(ctx.handle, batch, total_tokens, max_tokens))
 
 
 def gp_update_summaries(ctx: Context, qstate, q, slot, first_step, stream=None):

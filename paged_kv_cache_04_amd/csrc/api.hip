@@ -11,6 +11,7 @@
 struct gp_ctx {
   gp::Params p;
   int device = 0;
+  int num_cus = 256;
   int64_t* d_counters = nullptr;  // [3]
   int32_t* d_err = nullptr;       // [1], right after the counters
   int last_hip = 0;
@@ -19,6 +20,7 @@ struct gp_ctx {
   size_t ws_bytes = 0;
   int batch = 0;
   int64_t total_tokens = 0;
+  int64_t max_tokens = 0;
   std::vector<int32_t> pages;  // P per request at gp_demand time
   // kernel timing (gp_profile)
   bool profiling = false;
@@ -65,21 +67,23 @@ bool shape_supported(const gp::Params& p) {
 }
 
 gp_status check_batch(const gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
-                      int64_t* total_pages) {
+                      int64_t* total_pages, int64_t* max_pages_used) {
   if (!pool || !bt) return GP_ERR_INVALID_ARG;
   if (!pool->k_pool || !pool->v_pool || pool->num_pages < 1) return GP_ERR_INVALID_ARG;
   if (bt->batch < 1 || bt->max_pages < 1 || !bt->block_table || !bt->num_pages ||
       !bt->num_tokens || !bt->slot || !bt->position || !bt->num_pages_host)
     return GP_ERR_INVALID_ARG;
   if (bt->batch > gp::kMaxBatch) return GP_ERR_UNSUPPORTED;
-  int64_t tot = 0;
+  int64_t tot = 0, mx = 0;
   for (int r = 0; r < bt->batch; ++r) {
     const int32_t P = bt->num_pages_host[r];
     if (P < 1 || P > bt->max_pages) return GP_ERR_INVALID_ARG;
     tot += P;
+    mx = P > mx ? P : mx;
   }
   (void)c;
   *total_pages = tot;
+  *max_pages_used = mx;
   return GP_OK;
 }
 
@@ -113,6 +117,8 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
   if (!c) return GP_ERR_INVALID_ARG;
   c->p = p;
   hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&c->d_counters), 64);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, 64);
   if (e != hipSuccess) {
@@ -136,9 +142,10 @@ void gp_destroy(gp_ctx* c) {
   delete c;
 }
 
-size_t gp_workspace_bytes(const gp_ctx* c, int32_t batch, int64_t total_tokens) {
-  if (!c || batch < 1 || total_tokens < 0) return 0;
-  return gp::ws_layout(c->p, batch, total_tokens).total;
+size_t gp_workspace_bytes(const gp_ctx* c, int32_t batch, int64_t total_tokens,
+                          int64_t max_tokens) {
+  if (!c || batch < 1 || total_tokens < 0 || max_tokens < 0) return 0;
+  return gp::ws_layout(c->p, batch, total_tokens, max_tokens, c->num_cus * gp::kDemandBlocksPerCU).total;
 }
 
 gp_status gp_update_summaries(gp_ctx* c, float* qstate, const float* q, const int32_t* slot,
@@ -158,35 +165,34 @@ gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const fl
       !out->k_long || !out->decision)
     return GP_ERR_INVALID_ARG;
   if (!shape_supported(c->p)) return GP_ERR_UNSUPPORTED;
-  int64_t total_pages = 0;
-  gp_status st = check_batch(c, pool, bt, &total_pages);
+  int64_t total_pages = 0, max_pages_used = 0;
+  gp_status st = check_batch(c, pool, bt, &total_pages, &max_pages_used);
   if (st != GP_OK) return st;
   const int B = bt->batch;
   const int64_t total_tokens = total_pages * c->p.b;
-  const gp::WsLayout w = gp::ws_layout(c->p, B, total_tokens);
+  const int64_t max_tokens = max_pages_used * c->p.b;
+  const gp::WsLayout w = gp::ws_layout(c->p, B, total_tokens, max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   if (!ws || ws_bytes < w.total) return GP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed(c, GP_K_PLAN, s, [&] {
-    return gp::launch_plan(c->p, bt->num_pages, B, bt->max_pages, total_pages, ws, c->d_err, s);
+    return gp::launch_plan(c->p, w, bt->num_pages, B, bt->max_pages, total_pages, ws, c->d_err,
+                           s);
   });
   if (e == hipSuccess)
     e = timed(c, GP_K_QHAT, s, [&] {
-      return gp::launch_qhat(c->p, qstate, q_cur, rope, rope_rows, bt->slot, bt->position, B,
+      return gp::launch_qhat(c->p, w, qstate, q_cur, rope, rope_rows, bt->slot, bt->position, B,
                              ws, c->d_err, s);
     });
   if (e == hipSuccess)
-    e = timed(c, GP_K_SCORE, s, [&] {
-      return gp::launch_score(c->p, w, pool->k_pool, pool->num_pages, bt->block_table,
-                              bt->max_pages, B, ws, c->d_err, s);
-    });
-  if (e == hipSuccess)
-    e = timed(c, GP_K_ROWSTATS, s, [&] {
-      return gp::launch_rowstats(c->p, w, B, ws, out->k_short, out->k_long, out->abar, s);
+    e = timed(c, GP_K_DEMAND, s, [&] {
+      return gp::launch_demand(c->p, w, pool->k_pool, pool->num_pages, bt->block_table,
+                               bt->max_pages, B, ws, out->k_short, out->k_long, out->abar,
+                               c->d_err, s);
     });
   if (e == hipSuccess)
     e = timed(c, GP_K_DECIDE, s, [&] {
-      return gp::launch_decide(c->p, B, ws, out->k_short, out->k_long, out->k_diff, out->delta,
-                               out->decision, s);
+      return gp::launch_decide(c->p, w, B, ws, out->k_short, out->k_long, out->k_diff,
+                               out->delta, out->decision, s);
     });
   if (e != hipSuccess) {
     c->ws = nullptr;
@@ -196,6 +202,7 @@ gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const fl
   c->ws_bytes = ws_bytes;
   c->batch = B;
   c->total_tokens = total_tokens;
+  c->max_tokens = max_tokens;
   c->pages.assign(bt->num_pages_host, bt->num_pages_host + B);
   return GP_OK;
 }
@@ -236,7 +243,7 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
     const int64_t loc = (P - 1) * (kq < p.b ? kq : p.b) + (kq < p.b - p.R ? kq : p.b - p.R);
     if (loc > (P - 1) * p.b - p.R) return GP_ERR_UNSUPPORTED;
   }
-  const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens);
+  const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens, c->max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed(c, GP_K_SELECT, s, [&] {
     return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);

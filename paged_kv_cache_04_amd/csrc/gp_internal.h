@@ -17,6 +17,8 @@ constexpr int kPage = 256;
 constexpr int kGroup = 4;
 constexpr int kNQ = 2 * kGroup;
 constexpr int kMaxBatch = 1024;
+// Demand kernel: persistent workgroups per CU (each holds one row at a time).
+constexpr int kDemandBlocksPerCU = 1;
 constexpr uint64_t kWsMagic = 0x4750574b53503031ull;  // "GPWKSP01"
 
 // Fixed-point scale for exact, order-free sums of probabilities: values in
@@ -36,31 +38,39 @@ struct WsHeader {
   int32_t batch;
   int32_t valid;         // 1 once the plan kernel accepted the batch
   int64_t total_tokens;  // sum of N over the batch
-  int64_t pad[5];
+  int32_t row_counter;   // work queue of the demand kernel
+  int32_t pad0;
+  int64_t pad[4];
 };
 
+// Workspace: batch plan, calibrated summaries, per-token importance (read by
+// gp_compress_hold), dropped slots, and per-workgroup rings that hold one
+// row's logits and demand distributions at a time.
 struct WsLayout {
-  size_t header, page_off, qhat, logits, pmax, imp, keys, dropped, total;
-  int64_t rows, row_tokens, row_pages;
+  size_t header, page_off, req_order, qhat, ring_logits, ring_keys, imp, dropped, total;
+  int64_t rows, row_tokens, row_pages, ring_tokens, blocks;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(const Params& p, int B, int64_t total_tokens) {
+inline WsLayout ws_layout(const Params& p, int B, int64_t total_tokens, int64_t max_tokens,
+                          int blocks) {
   WsLayout w{};
   const int64_t lh = (int64_t)p.L * p.Hkv;
   w.rows = (int64_t)B * lh;
   w.row_tokens = lh * total_tokens;
   w.row_pages = lh * (total_tokens / p.b);
+  w.ring_tokens = max_tokens;
+  w.blocks = blocks;
   size_t o = 0;
-  w.header = o;   o = align256(o + sizeof(WsHeader));
-  w.page_off = o; o = align256(o + sizeof(int64_t) * (B + 1));
-  w.qhat = o;     o = align256(o + sizeof(float) * (size_t)w.rows * kNQ * kD);
-  w.logits = o;   o = align256(o + sizeof(float) * (size_t)w.row_tokens * kNQ);
-  w.pmax = o;     o = align256(o + sizeof(float) * (size_t)w.row_pages * kNQ);
-  w.imp = o;      o = align256(o + sizeof(float) * (size_t)w.row_tokens);
-  w.keys = o;     o = align256(o + sizeof(float) * (size_t)w.row_tokens * 2);
-  w.dropped = o;  o = align256(o + sizeof(int32_t) * (size_t)w.rows * p.b);
+  w.header = o;      o = align256(o + sizeof(WsHeader));
+  w.page_off = o;    o = align256(o + sizeof(int64_t) * (B + 1));
+  w.req_order = o;   o = align256(o + sizeof(int32_t) * B);
+  w.qhat = o;        o = align256(o + sizeof(float) * (size_t)w.rows * kNQ * kD);
+  w.ring_logits = o; o = align256(o + sizeof(float) * (size_t)blocks * max_tokens * kNQ);
+  w.ring_keys = o;   o = align256(o + sizeof(float) * (size_t)blocks * max_tokens * 2);
+  w.imp = o;         o = align256(o + sizeof(float) * (size_t)w.row_tokens);
+  w.dropped = o;     o = align256(o + sizeof(int32_t) * (size_t)w.rows * p.b);
   w.total = o;
   return w;
 }
@@ -97,21 +107,21 @@ __device__ __forceinline__ uint64_t fix40(float v) { return (uint64_t)(v * kFix)
 hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int32_t* slot,
                       const uint8_t* first, int B, int32_t* err, hipStream_t s);
 
-hipError_t launch_plan(const Params& p, const int32_t* num_pages_dev, int B, int max_pages,
-                       int64_t host_total_pages, void* ws, int32_t* err, hipStream_t s);
+hipError_t launch_plan(const Params& p, const WsLayout& w, const int32_t* num_pages_dev, int B,
+                       int max_pages, int64_t host_total_pages, void* ws, int32_t* err,
+                       hipStream_t s);
 
-hipError_t launch_qhat(const Params& p, const float* qstate, const float* qcur,
+hipError_t launch_qhat(const Params& p, const WsLayout& w, const float* qstate, const float* qcur,
                        const float* rope, int rope_rows, const int32_t* slot,
                        const int32_t* position, int B, void* ws, int32_t* err, hipStream_t s);
 
-hipError_t launch_score(const Params& p, const WsLayout& w, const uint16_t* k_pool,
-                        int pool_pages, const int32_t* block_table, int max_pages, int B,
-                        void* ws, int32_t* err, hipStream_t s);
+hipError_t launch_demand(const Params& p, const WsLayout& w, const uint16_t* k_pool,
+                         int pool_pages, const int32_t* block_table, int max_pages, int B,
+                         void* ws, int32_t* k_short, int32_t* k_long, float* abar, int32_t* err,
+                         hipStream_t s);
 
-hipError_t launch_rowstats(const Params& p, const WsLayout& w, int B, void* ws,
-                           int32_t* k_short, int32_t* k_long, float* abar, hipStream_t s);
-
-hipError_t launch_decide(const Params& p, int B, const void* ws, const int32_t* k_short,
+hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* ws,
+                         const int32_t* k_short,
                          const int32_t* k_long, int64_t* k_diff, double* delta,
                          int8_t* decision, hipStream_t s);
 

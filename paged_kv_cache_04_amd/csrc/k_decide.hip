@@ -50,10 +50,9 @@ __global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau,
   }
 }
 
-hipError_t launch_decide(const Params& p, int B, const void* ws, const int32_t* k_short,
-                         const int32_t* k_long, int64_t* k_diff, double* delta,
-                         int8_t* decision, hipStream_t s) {
-  const WsLayout w = ws_layout(p, B, 0);
+hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* ws,
+                         const int32_t* k_short, const int32_t* k_long, int64_t* k_diff,
+                         double* delta, int8_t* decision, hipStream_t s) {
   const char* base = static_cast<const char*>(ws);
   hipLaunchKernelGGL(k_decide, dim3(B), dim3(256), 0, s, p.L * p.Hkv, p.b, p.tau,
                      reinterpret_cast<const WsHeader*>(base + w.header),

@@ -1,0 +1,551 @@
+// A2-A4 fused per row: score every cached key of a (layer, KV head) row
+// against its 8 calibrated summary queries, form the attention distributions,
+// the per-token importance and the p-coverage demand of both views.
+// Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
+// Reasoning Serving" (arXiv 2609.03494): §3.1 Eq. 2, §3.2 Eq. 7, §3.3 Eq. 9,
+// App. E.1 ("Demand estimation at capacity boundaries").
+//
+// Persistent kernel, two 8-wave workgroups per CU (one can stream keys while
+// the other works on its row's distributions).  Workgroups pull rows from
+// a queue ordered longest request first.  Per row:
+//  1. score: each wave takes every 16th 64-key tile of the row and pipelines
+//     it in two halves (key elements 0-63, then 64-127): while it multiplies
+//     one half from its private LDS stage (half rows padded to 144 B so the
+//     lanes' 16-byte row reads hit distinct banks), the 8 coalesced 16-byte
+//     loads of the next half are in flight into registers.  Each lane scores
+//     one key with 8 serial fmaf chains over j = 0..127 in index order (the
+//     fp32 contract shared with the CPU reference); the summary values come
+//     by scalar loads, one quad of 4 elements x 8 queries at a time, requested
+//     a quad ahead.  The 8 logits per key go to the workgroup's own logits
+//     ring, which it overwrites row after row, so they are read back from
+//     cache instead of making a round trip through HBM;
+//  2. maxima over C_t = [0, N - b) and over all slots; exact normalisers
+//     Z = sum floor(exp(l - m) * 2^40) (uint64, order-free);
+//  3. a = exp(l - m) * (1 / Z), GQA mean of the 4 heads of each view, for C_t
+//     and for all slots; s = max of the full-cache means (Eq. 9) to the
+//     importance array; demand means to the key ring; first radix digit
+//     (bits 30..20 of the fp32 pattern: exponent and 3 mantissa bits) of each
+//     view histogrammed in LDS with counts and masses floor(abar * 2^40);
+//  4. D_p per view: the bucket where the descending prefix mass reaches p,
+//     then the remaining 20 bits resolved on that bucket's members only
+//     (collected into LDS, or scanned in the key ring when too many), then
+//     D_p = (count above) + ceil(remaining mass / member mass).
+#include "gp_internal.h"
+
+namespace gp {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDW = 16 / kDemandBlocksPerCU;  // waves per workgroup
+constexpr int kDT = kDW * 64;                 // threads
+constexpr int kHalfPad = 144;                 // bytes per staged half row
+constexpr int kWaveStage = 64 * kHalfPad;     // bytes per wave
+constexpr int kLdsBytes = kDW * kWaveStage;   // 147456, reused after scoring
+constexpr int kH1 = 2048;                     // first-digit buckets
+constexpr int kH2 = 1024;                     // second/third-digit buckets
+constexpr int kListCap = (kLdsBytes - 2 * kH1 * 12 - kH2 * 12) / 4;  // boundary members in LDS
+
+// acc[qi] += q[qi][e] * k[e] for e = 0..3 in order (4 bf16 keys in k).
+__device__ __forceinline__ void fma_quad(float* acc, const float* q, u32x2 k) {
+  const float k0 = bf16_lo(k.x), k1 = bf16_hi(k.x), k2 = bf16_lo(k.y), k3 = bf16_hi(k.y);
+#pragma unroll
+  for (int qi = 0; qi < kNQ; ++qi) acc[qi] = __builtin_fmaf(q[qi * 4 + 0], k0, acc[qi]);
+#pragma unroll
+  for (int qi = 0; qi < kNQ; ++qi) acc[qi] = __builtin_fmaf(q[qi * 4 + 1], k1, acc[qi]);
+#pragma unroll
+  for (int qi = 0; qi < kNQ; ++qi) acc[qi] = __builtin_fmaf(q[qi * 4 + 2], k2, acc[qi]);
+#pragma unroll
+  for (int qi = 0; qi < kNQ; ++qi) acc[qi] = __builtin_fmaf(q[qi * 4 + 3], k3, acc[qi]);
+}
+
+__device__ __forceinline__ void wave_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const unsigned lo = __shfl_xor((unsigned)v, m);
+  const unsigned hi = __shfl_xor((unsigned)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int off) {
+  const unsigned lo = __shfl_down((unsigned)v, off);
+  const unsigned hi = __shfl_down((unsigned)(v >> 32), off);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += shfl_xor_u64(v, m);
+  return v;
+}
+
+// Wave 0: over nb buckets (cnt, mass), find the largest bucket d with
+// p_den * (m_above + mass of buckets >= d) >= target; returns through *d_out
+// the bucket and updates m_above / c_above to the buckets above it.
+template <int NB>
+__device__ __forceinline__ void scan_desc(const uint32_t* cnt, const uint64_t* mass,
+                                          uint64_t target, uint32_t p_den, uint64_t& m_above,
+                                          uint32_t& c_above, int& d_out) {
+  constexpr int PER = NB / 64;
+  const int lane = threadIdx.x & 63;
+  uint64_t lm = 0;
+  uint32_t lc = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    lm += mass[lane * PER + u];
+    lc += cnt[lane * PER + u];
+  }
+  uint64_t sm = lm;
+  uint32_t sc = lc;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t vm = shfl_down_u64(sm, off);
+    const uint32_t vc = __shfl_down(sc, off);
+    if (lane + off < 64) {
+      sm += vm;
+      sc += vc;
+    }
+  }
+  uint64_t cum = m_above + (sm - lm);
+  uint32_t ccum = c_above + (sc - lc);
+  int best = -1;
+  uint64_t best_m = 0;
+  uint32_t best_c = 0;
+  for (int u = PER - 1; u >= 0; --u) {
+    const uint64_t before = cum;
+    const uint32_t cbefore = ccum;
+    cum += mass[lane * PER + u];
+    ccum += cnt[lane * PER + u];
+    if (best < 0 && cum * (uint64_t)p_den >= target) {
+      best = lane * PER + u;
+      best_m = before;
+      best_c = cbefore;
+    }
+  }
+  const unsigned long long ok = __ballot(best >= 0);
+  const int hl = 63 - __clzll(ok);
+  d_out = __shfl(best, hl);
+  const unsigned lo = __shfl((unsigned)best_m, hl), hi = __shfl((unsigned)(best_m >> 32), hl);
+  m_above = ((uint64_t)hi << 32) | lo;
+  c_above = __shfl(best_c, hl);
+}
+
+struct DemandArgs {
+  const uint16_t* k_pool;
+  int pool_pages;
+  const int32_t* block_table;
+  int max_pages;
+  int L, Hkv, B, b, p_num, p_den;
+  const WsHeader* hdr;
+  const int64_t* page_off;
+  const int32_t* req_order;
+  int32_t* row_counter;
+  const float* qhat;
+  float* ring_logits;   // [blocks][ring_tokens][8]
+  float* ring_keys;     // [blocks][ring_tokens][2]
+  int64_t ring_tokens;
+  float* imp;
+  int32_t* k_short;
+  int32_t* k_long;
+  float* abar;
+  int32_t* err;
+};
+
+__global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __restrict__ qhat,
+                                               const uint16_t* __restrict__ k_pool) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ float s_wmax[kDW][2][kNQ];
+  __shared__ float s_m[2][kNQ];
+  __shared__ float s_rho[2][kNQ];
+  __shared__ uint64_t s_red[kDW][2 * kNQ];
+  __shared__ uint64_t s_W[2];
+  __shared__ int s_item;
+  __shared__ int s_list_n;
+  __shared__ int s_dig;
+  __shared__ uint64_t s_mab;
+  __shared__ uint32_t s_cab;
+  if (!a.hdr->valid) return;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int LH = a.L * a.Hkv;
+  const int64_t n_items = (int64_t)a.B * LH;
+  float* lg = a.ring_logits + (int64_t)blockIdx.x * a.ring_tokens * kNQ;
+  float* rk = a.ring_keys + (int64_t)blockIdx.x * a.ring_tokens * 2;
+  unsigned char* my = lds + w * kWaveStage;
+  // LDS views used after scoring
+  uint32_t* h1c = reinterpret_cast<uint32_t*>(lds);             // [2][kH1]
+  uint64_t* h1m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 4);  // [2][kH1]
+  uint32_t* h2c = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 12);  // [kH2]
+  uint64_t* h2m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 12 + kH2 * 4);  // [kH2]
+  uint32_t* list = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 12 + kH2 * 12);  // [kListCap]
+
+  while (true) {
+    if (t == 0) s_item = atomicAdd(a.row_counter, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= n_items) break;
+    const int r = __builtin_amdgcn_readfirstlane(a.req_order[item / LH]);
+    const int lh = __builtin_amdgcn_readfirstlane(item % LH);
+    const int row = __builtin_amdgcn_readfirstlane(r * LH + lh);
+    const int l = __builtin_amdgcn_readfirstlane(lh / a.Hkv);
+    const int h = __builtin_amdgcn_readfirstlane(lh % a.Hkv);
+    const int64_t P = a.page_off[r + 1] - a.page_off[r];
+    const int64_t N = P * kPage, ndem = N - kPage;
+    const int64_t row_tok = (int64_t)LH * a.page_off[r] * kPage + (int64_t)lh * N;
+    const float* __restrict__ qv = qhat + (int64_t)row * (kNQ * kD);
+
+    // ---- 1. score -------------------------------------------------------------
+    float md[kNQ], ml[kNQ];
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) md[q] = ml[q] = -INFINITY;
+    const int n_tiles = (int)(4 * P);
+    if (w < n_tiles) {
+      auto tile_base = [&](int tt, bool& bad) -> const unsigned char* {
+        const int pg = tt >> 2;
+        const int page = a.block_table[(int64_t)r * a.max_pages + pg];
+        bad = page < 0 || page >= a.pool_pages;
+        return reinterpret_cast<const unsigned char*>(
+            k_pool + ((((int64_t)l * a.pool_pages + (bad ? 0 : page)) * a.Hkv + h) * kPage +
+                        (tt & 3) * 64) * kD);
+      };
+      auto issue = [&](const unsigned char* base, int half, u32x4* v) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = i * 8 + (lane >> 3);
+          v[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(base + key * 256 + half * 128 + (lane & 7) * 16));
+        }
+      };
+      int tt = w;
+      bool bad;
+      const unsigned char* src = tile_base(tt, bad);
+      u32x4 v[8];
+      issue(src, 0, v);
+      while (true) {
+        const int tcur = tt;
+        const bool cur_bad = bad;
+        const unsigned char* cur_src = src;
+        bool has_next = false;
+        float acc[kNQ];
+#pragma unroll
+        for (int qi = 0; qi < kNQ; ++qi) acc[qi] = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = i * 8 + (lane >> 3);
+            *reinterpret_cast<u32x4*>(my + key * kHalfPad + (lane & 7) * 16) = v[i];
+          }
+          wave_order();
+          if (half == 0) {
+            issue(cur_src, 1, v);
+          } else {
+            has_next = tt + kDW < n_tiles;
+            if (has_next) {
+              tt += kDW;
+              src = tile_base(tt, bad);
+              issue(src, 0, v);
+            }
+          }
+          if (!cur_bad) {
+            const unsigned char* rowp = my + lane * kHalfPad;
+            const float* qh = qv + half * 16 * 32;
+            float qa[32], qb[32];
+            u32x4 kc, kn;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) qa[i] = qh[i];
+            kc = *reinterpret_cast<const u32x4*>(rowp);
+#pragma unroll
+            for (int ch = 0; ch < 8; ++ch) {
+              __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): quad 2ch and chunk ch ready
+#pragma unroll
+              for (int i = 0; i < 32; ++i) qb[i] = qh[(2 * ch + 1) * 32 + i];
+              fma_quad(acc, qa, kc.xy);
+              __builtin_amdgcn_s_waitcnt(0xc07f);  // quad 2ch+1 ready
+              if (ch + 1 < 8) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) qa[i] = qh[(2 * ch + 2) * 32 + i];
+                kn = *reinterpret_cast<const u32x4*>(rowp + (ch + 1) * 16);
+              }
+              fma_quad(acc, qb, kc.zw);
+              kc = kn;
+            }
+          }
+          wave_order();
+        }
+        if (cur_bad && lane == 0) atomicOr(a.err, GP_DEVERR_PAGE);
+        const int64_t tok = (int64_t)tcur * 64 + lane;
+        float4* out = reinterpret_cast<float4*>(lg + tok * kNQ);
+        out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if ((tcur >> 2) < P - 1) {
+#pragma unroll
+          for (int q = 0; q < kNQ; ++q) md[q] = fmaxf(md[q], acc[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kNQ; ++q) ml[q] = fmaxf(ml[q], acc[q]);
+        }
+        if (!has_next) break;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        md[q] = fmaxf(md[q], __shfl_xor(md[q], off));
+        ml[q] = fmaxf(ml[q], __shfl_xor(ml[q], off));
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        s_wmax[w][0][q] = md[q];
+        s_wmax[w][1][q] = ml[q];
+      }
+    }
+    __syncthreads();  // logits visible to the block, maxima gathered
+    if (t < kNQ) {
+      float d = -INFINITY, e = -INFINITY;
+      for (int ww = 0; ww < kDW; ++ww) {
+        d = fmaxf(d, s_wmax[ww][0][t]);
+        e = fmaxf(e, s_wmax[ww][1][t]);
+      }
+      s_m[0][t] = d;
+      s_m[1][t] = fmaxf(d, e);
+    }
+    // clear the first-digit histograms (the stage is free now)
+    for (int k = t; k < 2 * kH1; k += kDT) {
+      h1c[k] = 0;
+      h1m[k] = 0;
+    }
+    __syncthreads();
+    float mdem[kNQ], mall[kNQ];
+    bool same[kNQ];
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+      mdem[q] = s_m[0][q];
+      mall[q] = s_m[1][q];
+      same[q] = mdem[q] == mall[q];
+    }
+
+    // ---- 2. exact fixed-point normalisers ----------------------------------------
+    {
+      uint64_t zd[kNQ], za[kNQ];
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) zd[q] = za[q] = 0;
+      for (int64_t i = t; i < N; i += kDT) {
+        const float4* lp = reinterpret_cast<const float4*>(lg + i * kNQ);
+        const float4 x0 = lp[0], x1 = lp[1];
+        const float lv[kNQ] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const bool dem = i < ndem;
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) {
+          const float ea = gp_exp(lv[q] - mall[q]);
+          za[q] += fix40(ea);
+          if (dem) zd[q] += fix40(same[q] ? ea : gp_exp(lv[q] - mdem[q]));
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 2 * kNQ; ++v) {
+        const uint64_t s = wave_sum_u64(v < kNQ ? zd[v] : za[v - kNQ]);
+        if (lane == 0) s_red[w][v] = s;
+      }
+      __syncthreads();
+      if (t < 2 * kNQ) {
+        uint64_t z = 0;
+        for (int ww = 0; ww < kDW; ++ww) z += s_red[ww][t];
+        const float zf = (float)z * kFixInv;
+        if (t < kNQ) s_rho[0][t] = ndem > 0 ? 1.0f / zf : 0.0f;
+        else s_rho[1][t - kNQ] = 1.0f / zf;
+      }
+      __syncthreads();
+    }
+
+    // ---- 3. distributions, importance, demand keys, first-digit histograms -----
+    {
+      float rd[kNQ], ra[kNQ];
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        rd[q] = s_rho[0][q];
+        ra[q] = s_rho[1][q];
+      }
+      uint64_t ws0 = 0, ws1 = 0;
+      for (int64_t i = t; i < N; i += kDT) {
+        const float4* lp = reinterpret_cast<const float4*>(lg + i * kNQ);
+        const float4 x0 = lp[0], x1 = lp[1];
+        const float lv[kNQ] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const bool dem = i < ndem;
+        float aa[2], ad[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          float sa = 0.0f, sd = 0.0f;
+#pragma unroll
+          for (int g = 0; g < kGroup; ++g) {
+            const int q = x * kGroup + g;
+            const float ea = gp_exp(lv[q] - mall[q]);
+            sa = sa + ea * ra[q];
+            if (dem) {
+              const float ed = same[q] ? ea : gp_exp(lv[q] - mdem[q]);
+              sd = sd + ed * rd[q];
+            }
+          }
+          aa[x] = sa / (float)kGroup;
+          ad[x] = sd / (float)kGroup;
+        }
+        a.imp[row_tok + i] = fmaxf(aa[0], aa[1]);
+        if (a.abar) reinterpret_cast<float2*>(a.abar)[row_tok + i] = make_float2(aa[0], aa[1]);
+        if (dem) {
+          reinterpret_cast<float2*>(rk)[i] = make_float2(ad[0], ad[1]);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const uint32_t key = __float_as_uint(ad[x]);
+            const uint64_t wm = fix40(ad[x]);
+            atomicAdd(&h1c[x * kH1 + (key >> 20)], 1u);
+            atomicAdd((unsigned long long*)&h1m[x * kH1 + (key >> 20)], (unsigned long long)wm);
+          }
+          ws0 += fix40(ad[0]);
+          ws1 += fix40(ad[1]);
+        }
+      }
+      ws0 = wave_sum_u64(ws0);
+      ws1 = wave_sum_u64(ws1);
+      if (lane == 0) {
+        s_red[w][0] = ws0;
+        s_red[w][1] = ws1;
+      }
+      __syncthreads();
+      if (t < 2) {
+        uint64_t s = 0;
+        for (int ww = 0; ww < kDW; ++ww) s += s_red[ww][t];
+        s_W[t] = s;
+      }
+      __syncthreads();
+    }
+
+    // ---- 4. D_p of each view ------------------------------------------------------
+    for (int x = 0; x < 2; ++x) {
+      int32_t* outp = x == 0 ? a.k_short : a.k_long;
+      if (ndem <= 0) {
+        if (t == 0) outp[row] = 0;
+        continue;
+      }
+      const uint64_t target = s_W[x] * (uint64_t)a.p_num;
+      if (w == 0) {
+        uint64_t mab = 0;
+        uint32_t cab = 0;
+        int d1;
+        scan_desc<kH1>(h1c + x * kH1, h1m + x * kH1, target, (uint32_t)a.p_den, mab, cab, d1);
+        if (lane == 0) {
+          s_dig = d1;
+          s_mab = mab;
+          s_cab = cab;
+          s_list_n = 0;
+        }
+      }
+      __syncthreads();
+      const uint32_t d1 = (uint32_t)s_dig;
+      const uint32_t cnt1 = h1c[x * kH1 + d1];
+      uint32_t prefix = d1 << 20;
+      const bool in_lds = cnt1 <= (uint32_t)kListCap;
+      if (in_lds) {
+        for (int64_t i = t; i < ndem; i += kDT) {
+          const uint32_t key = __float_as_uint(rk[i * 2 + x]);
+          if ((key >> 20) == d1) list[atomicAdd(&s_list_n, 1)] = key;
+        }
+      }
+      __syncthreads();
+      // digits 2 (bits 19..10) and 3 (bits 9..0)
+      for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        const uint32_t mask = pass == 0 ? 0xfff00000u : 0xfffffc00u;
+        for (int k = t; k < kH2; k += kDT) {
+          h2c[k] = 0;
+          h2m[k] = 0;
+        }
+        __syncthreads();
+        if (in_lds) {
+          const int n = s_list_n;
+          for (int k = t; k < n; k += kDT) {
+            const uint32_t key = list[k];
+            if ((key & mask) == prefix) {
+              const uint32_t dig = (key >> shift) & (kH2 - 1);
+              atomicAdd(&h2c[dig], 1u);
+              atomicAdd((unsigned long long*)&h2m[dig],
+                        (unsigned long long)fix40(__uint_as_float(key)));
+            }
+          }
+        } else {
+          for (int64_t i = t; i < ndem; i += kDT) {
+            const uint32_t key = __float_as_uint(rk[i * 2 + x]);
+            if ((key & mask) == prefix) {
+              const uint32_t dig = (key >> shift) & (kH2 - 1);
+              atomicAdd(&h2c[dig], 1u);
+              atomicAdd((unsigned long long*)&h2m[dig],
+                        (unsigned long long)fix40(__uint_as_float(key)));
+            }
+          }
+        }
+        __syncthreads();
+        if (w == 0) {
+          uint64_t mab = s_mab;
+          uint32_t cab = s_cab;
+          int dd;
+          scan_desc<kH2>(h2c, h2m, target, (uint32_t)a.p_den, mab, cab, dd);
+          if (lane == 0) {
+            s_dig = dd;
+            s_mab = mab;
+            s_cab = cab;
+          }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_dig << shift;
+      }
+      if (t == 0) {
+        const uint64_t wt = fix40(__uint_as_float(prefix));
+        const uint64_t need = target - s_mab * (uint64_t)a.p_den;
+        const uint64_t den = wt * (uint64_t)a.p_den;
+        outp[row] = (int32_t)(s_cab + (need + den - 1) / den);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_demand(const Params& p, const WsLayout& w, const uint16_t* k_pool,
+                         int pool_pages, const int32_t* block_table, int max_pages, int B,
+                         void* ws, int32_t* k_short, int32_t* k_long, float* abar, int32_t* err,
+                         hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  DemandArgs a;
+  a.k_pool = k_pool;
+  a.pool_pages = pool_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.L = p.L;
+  a.Hkv = p.Hkv;
+  a.B = B;
+  a.b = p.b;
+  a.p_num = p.p_num;
+  a.p_den = p.p_den;
+  a.hdr = reinterpret_cast<const WsHeader*>(base + w.header);
+  a.page_off = reinterpret_cast<const int64_t*>(base + w.page_off);
+  a.req_order = reinterpret_cast<const int32_t*>(base + w.req_order);
+  a.row_counter = &reinterpret_cast<WsHeader*>(base + w.header)->row_counter;
+  a.qhat = reinterpret_cast<const float*>(base + w.qhat);
+  a.ring_logits = reinterpret_cast<float*>(base + w.ring_logits);
+  a.ring_keys = reinterpret_cast<float*>(base + w.ring_keys);
+  a.ring_tokens = w.ring_tokens;
+  a.imp = reinterpret_cast<float*>(base + w.imp);
+  a.k_short = k_short;
+  a.k_long = k_long;
+  a.abar = abar;
+  a.err = err;
+  hipLaunchKernelGGL(k_demand, dim3((unsigned)w.blocks), dim3(kDT), 0, s, a, a.qhat, a.k_pool);
+  return hipGetLastError();
+}
+
+}  // namespace gp

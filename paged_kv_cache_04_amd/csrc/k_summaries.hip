@@ -66,17 +66,21 @@ hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int3
 
 // ---------------------------------------------------------------------------
 // Batch plan: prefix sums of the device page counts (page_off[r] = sum of P
-// over requests before r).  The batch is accepted (header.valid = 1) only if
-// every count lies in [1, max_pages] and the total equals the host's; every
-// later kernel of the event exits at once on a rejected batch, so a stale
-// host mirror can never send a kernel outside the workspace.
+// over requests before r), the demand kernel's work order (requests by page
+// count, largest first, ties by index) and its queue counter.  The batch is
+// accepted (header.valid = 1) only if every count lies in [1, max_pages], no
+// request is longer than the workspace's per-row rings and the total equals
+// the host's; every later kernel of the event exits at once on a rejected
+// batch, so a stale host mirror can never send a kernel outside the workspace.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_pages, int B,
                                                int max_pages, int64_t host_total_pages, int b,
-                                               WsHeader* __restrict__ hdr,
+                                               int64_t ring_tokens, WsHeader* __restrict__ hdr,
                                                int64_t* __restrict__ page_off,
+                                               int32_t* __restrict__ req_order,
                                                int32_t* __restrict__ err) {
   __shared__ int64_t buf[kMaxBatch];
+  __shared__ int32_t pages[kMaxBatch];
   __shared__ int bad;
   const int t = threadIdx.x;
   if (t == 0) bad = 0;
@@ -84,8 +88,9 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
   int64_t v = 0;
   if (t < B) {
     const int P = num_pages[t];
-    if (P < 1 || P > max_pages) atomicOr(&bad, 1);
+    if (P < 1 || P > max_pages || (int64_t)P * b > ring_tokens) atomicOr(&bad, 1);
     v = P;
+    pages[t] = P;
   }
   buf[t] = v;
   __syncthreads();
@@ -95,7 +100,13 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
     buf[t] += add;
     __syncthreads();
   }
-  if (t < B) page_off[t + 1] = buf[t];
+  if (t < B) {
+    page_off[t + 1] = buf[t];
+    const int32_t mine = pages[t];
+    int rank = 0;
+    for (int u = 0; u < B; ++u) rank += (pages[u] > mine) || (pages[u] == mine && u < t);
+    req_order[rank] = t;
+  }
   if (t == 0) {
     page_off[0] = 0;
     const int64_t total = buf[B - 1];
@@ -103,18 +114,21 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
     hdr->magic = kWsMagic;
     hdr->batch = B;
     hdr->total_tokens = total * b;
+    hdr->row_counter = 0;
     hdr->valid = ok;
     if (!ok) atomicOr(err, GP_DEVERR_PAGES);
   }
 }
 
-hipError_t launch_plan(const Params& p, const int32_t* num_pages_dev, int B, int max_pages,
-                       int64_t host_total_pages, void* ws, int32_t* err, hipStream_t s) {
-  const WsLayout w = ws_layout(p, B, host_total_pages * p.b);
+hipError_t launch_plan(const Params& p, const WsLayout& w, const int32_t* num_pages_dev, int B,
+                       int max_pages, int64_t host_total_pages, void* ws, int32_t* err,
+                       hipStream_t s) {
   char* base = static_cast<char*>(ws);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(kMaxBatch), 0, s, num_pages_dev, B, max_pages,
-                     host_total_pages, p.b, reinterpret_cast<WsHeader*>(base + w.header),
-                     reinterpret_cast<int64_t*>(base + w.page_off), err);
+                     host_total_pages, p.b, w.ring_tokens,
+                     reinterpret_cast<WsHeader*>(base + w.header),
+                     reinterpret_cast<int64_t*>(base + w.page_off),
+                     reinterpret_cast<int32_t*>(base + w.req_order), err);
   return hipGetLastError();
 }
 
@@ -125,10 +139,10 @@ hipError_t launch_plan(const Params& p, const int32_t* num_pages_dev, int B, int
 //   gamma = sqrt(ss(q_t) / ss(qbar)) (serial fmaf sums of squares; 0 when
 //   ss(qbar) = 0), qtilde = gamma * qbar, rotate-half rotary at the current
 //   position with the caller's (cos, sin) row, times 1/sqrt(d).
-// Output layout per row (request, layer, KV head): [16 chunks][8 queries][8],
+// Output layout per row (request, layer, KV head): [32 quads][8 queries][4],
 // query index x * 4 + g for the g-th query head of the KV head (GQA grouping
-// of consecutive query heads); element j sits in chunk j / 8 at j % 8, so the
-// scoring kernel reads the 64 values of one 8-element key chunk contiguously.
+// of consecutive query heads); element j sits in quad j / 4 at j % 4, so the
+// scoring kernel reads the 32 values of one 4-element key quad contiguously.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_qhat(const float* __restrict__ qstate,
                                               const float* __restrict__ qcur,
@@ -172,16 +186,14 @@ __global__ __launch_bounds__(256) void k_qhat(const float* __restrict__ qstate,
     const float y1 = __builtin_fmaf(a, c, -(c2 * sn));
     const float y2 = __builtin_fmaf(c2, c, a * sn);
     const int j2 = j + half;
-    out[(j / 8) * 64 + qi * 8 + (j % 8)] = y1 * scale;
-    out[(j2 / 8) * 64 + qi * 8 + (j2 % 8)] = y2 * scale;
+    out[(j / 4) * 32 + qi * 4 + (j % 4)] = y1 * scale;
+    out[(j2 / 4) * 32 + qi * 4 + (j2 % 4)] = y2 * scale;
   }
 }
 
-hipError_t launch_qhat(const Params& p, const float* qstate, const float* qcur,
+hipError_t launch_qhat(const Params& p, const WsLayout& w, const float* qstate, const float* qcur,
                        const float* rope, int rope_rows, const int32_t* slot,
                        const int32_t* position, int B, void* ws, int32_t* err, hipStream_t s) {
-  // layout offsets of header and qhat do not depend on the token count
-  const WsLayout w = ws_layout(p, B, 0);
   char* base = static_cast<char*>(ws);
   hipLaunchKernelGGL(k_qhat, dim3((unsigned)(B * p.L)), dim3(256), 0, s, qstate, qcur, rope,
                      rope_rows, slot, position, p.L, p.M, p.Hq, p.Hkv,

@@ -25,9 +25,10 @@ class BoundaryRunner:
         dev = qstate.device
         B = batch.block_table.shape[0]
         total_tokens = int(batch.num_pages_host.astype(np.int64).sum()) * cfg.page_size
+        max_tokens = int(batch.num_pages_host.max()) * cfg.page_size
         self.total_tokens = total_tokens
         row_tokens = cfg.num_layers * cfg.num_kv_heads * total_tokens
-        self.ws = torch.empty(gb.gp_workspace_bytes(self.ctx, B, total_tokens), dtype=torch.uint8,
+        self.ws = torch.empty(gb.gp_workspace_bytes(self.ctx, B, total_tokens, max_tokens), dtype=torch.uint8,
                               device=dev)
         self.out = gb.DemandOut.empty(cfg, B, dev, row_tokens if want_abar else None)
         self.action = torch.empty(B, dtype=torch.int8, device=dev)
