@@ -18,7 +18,10 @@ constexpr int kGroup = 4;
 constexpr int kNQ = 2 * kGroup;
 constexpr int kMaxBatch = 1024;
 // Demand kernel: persistent workgroups per CU (each holds one row at a time).
-constexpr int kDemandBlocksPerCU = 1;
+#ifndef GP_DEMAND_BLOCKS_PER_CU
+#define GP_DEMAND_BLOCKS_PER_CU 1
+#endif
+constexpr int kDemandBlocksPerCU = GP_DEMAND_BLOCKS_PER_CU;
 constexpr uint64_t kWsMagic = 0x4750574b53503031ull;  // "GPWKSP01"
 
 // Fixed-point scale for exact, order-free sums of probabilities: values in
@@ -86,7 +89,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // so all later values stay normal fp32 numbers.
 __device__ __forceinline__ float gp_exp(float x) {
   const float n = __builtin_rintf(x * 0x1.715476p+0f);
-  if (n < -100.0f) return 0.0f;
   float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
   r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
   float p = 1.0f / 720.0f;
@@ -96,7 +98,10 @@ __device__ __forceinline__ float gp_exp(float x) {
   p = __builtin_fmaf(p, r, 0.5f);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  return p * __uint_as_float((uint32_t)(127 + (int)n) << 23);
+  // 2^n by the exponent field (n clamped so the conversion stays in range;
+  // below n = -100 the select returns 0, branch-free).
+  const float y = p * __uint_as_float((uint32_t)(127 + (int)fmaxf(n, -127.0f)) << 23);
+  return n < -100.0f ? 0.0f : y;
 }
 
 // Mass of a probability in 2^-40 units (exact: v * 2^40 <= 2^40).

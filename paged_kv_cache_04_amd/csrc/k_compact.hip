@@ -5,11 +5,12 @@
 //
 // Kept slots keep their order and move to destination j = slot - #(dropped
 // before slot); for destination j the source is j + #{k : d_k - k <= j},
-// found by binary search over the 256 sorted dropped slots d_k.  Slots before
-// the first dropped one stay where they are.  Each source lies at most b
-// slots after its destination, so the workgroup walks destinations in
-// 256-row chunks: it loads a whole chunk into registers, waits for the loads
-// and barriers, then stores.  A chunk's stores land below every later
+// found by binary search over the 256 sorted dropped slots d_k (one search
+// per destination row, kept with both addresses in a per-chunk table).
+// Slots before the first dropped one stay where they are.  Each source lies
+// at most b slots after its destination, so the workgroup walks destinations
+// in 256-row chunks: it loads a whole chunk into registers, waits for the
+// loads and barriers, then stores.  A chunk's stores land below every later
 // chunk's sources, and every earlier chunk has finished reading, so the
 // in-place move needs no copy of the row.  K and V rows, and different rows,
 // are disjoint and run as separate workgroups.
@@ -34,6 +35,8 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
                                                  int32_t* __restrict__ err) {
   __shared__ int32_t gap[kPage];
   __shared__ int32_t pg[kMaxPages];
+  __shared__ int64_t s_src[2][kCT];
+  __shared__ int64_t s_dst[2][kCT];
   __shared__ int bad;
   if (!hdr->valid) return;
   const int LH = L * Hkv;
@@ -65,21 +68,32 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
   };
   const int end = (int)((P - 1) * b);
   const int d0 = gap[0] > 0 ? gap[0] : 0;
-  for (int c0 = d0; c0 < end; c0 += kCT) {
-    u32x4 v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int piece = u * kCT + t;
-      const int drow = c0 + (piece >> 4), part = piece & 15;
+  int par = 0;
+  for (int c0 = d0; c0 < end; c0 += kCT, par ^= 1) {
+    // source and destination offsets of the chunk's 256 destination rows,
+    // one binary search per thread (tables alternate between two buffers so
+    // the next chunk's tables never overwrite ones still being read)
+    {
+      const int drow = c0 + t;
       if (drow < end) {
         int lo = 0, hi = kPage;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (gap[mid] <= drow) lo = mid + 1; else hi = mid;
         }
-        const int src = drow + lo;
-        v[u] = *reinterpret_cast<const u32x4*>(pool + slot_base(src) + part * 8);
+        s_src[par][t] = slot_base(drow + lo);
+        s_dst[par][t] = slot_base(drow);
       }
+    }
+    __syncthreads();
+    const int nrows = end - c0 < kCT ? end - c0 : kCT;
+    u32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int piece = u * kCT + t;
+      const int ri = piece >> 4, part = piece & 15;
+      if (ri < nrows)
+        v[u] = *reinterpret_cast<const u32x4*>(pool + s_src[par][ri] + part * 8);
     }
     // every source of this chunk must be read before any of its stores
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -87,8 +101,8 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int piece = u * kCT + t;
-      const int drow = c0 + (piece >> 4), part = piece & 15;
-      if (drow < end) *reinterpret_cast<u32x4*>(pool + slot_base(drow) + part * 8) = v[u];
+      const int ri = piece >> 4, part = piece & 15;
+      if (ri < nrows) *reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8) = v[u];
     }
   }
   if (lh == 0 && which == 0 && t == 0) num_tokens[r] = end;
