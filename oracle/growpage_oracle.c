@@ -357,12 +357,17 @@ void orc_grow(const int8_t* decision, int B, int32_t* block_table,
  * Pins: count, window, per-block quota, dominance of picks over drops,
  * equality with a plain sorted top-K when k_loc = 0.
  * ---------------------------------------------------------------------- */
-static const float* g_sel_s;
-static int cmp_slot_by_key_desc(const void* a, const void* b) {
-  int i = *(const int*)a, j = *(const int*)b;
-  float si = g_sel_s[i], sj = g_sel_s[j];
-  if (si != sj) return si > sj ? -1 : 1;
-  return i > j ? -1 : (i < j);
+typedef struct {
+  float s;
+  int slot;
+} orc_cand;
+
+/* larger s first; equal s, larger slot (newer token) first */
+static int cmp_cand_desc(const void* a, const void* b) {
+  const orc_cand* x = (const orc_cand*)a;
+  const orc_cand* y = (const orc_cand*)b;
+  if (x->s != y->s) return x->s > y->s ? -1 : 1;
+  return x->slot > y->slot ? -1 : (x->slot < y->slot);
 }
 
 int orc_select(const float* abar_all, int N, int b, int R, int k_loc,
@@ -372,30 +377,37 @@ int orc_select(const float* abar_all, int N, int b, int R, int k_loc,
   const int kt = (P - 1) * b - R;
   float* s = (float*)malloc(sizeof(float) * (size_t)N);
   for (int i = 0; i < N; ++i) s[i] = fmaxf(abar_all[(size_t)i * 2], abar_all[(size_t)i * 2 + 1]);
-  int* idx = (int*)malloc(sizeof(int) * (size_t)(nc > 0 ? nc : 1));
+  orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(nc > 0 ? nc : 1));
   memset(keep, 0, (size_t)N);
-  g_sel_s = s;
   int nloc = 0;
   for (int j = 0; j * b < nc; ++j) {
     int lo = j * b, hi = (j + 1) * b < nc ? (j + 1) * b : nc, n = 0;
-    for (int i = lo; i < hi; ++i) idx[n++] = i;
-    qsort(idx, (size_t)n, sizeof(int), cmp_slot_by_key_desc);
+    for (int i = lo; i < hi; ++i) {
+      c[n].s = s[i];
+      c[n].slot = i;
+      ++n;
+    }
+    qsort(c, (size_t)n, sizeof(orc_cand), cmp_cand_desc);
     int take = k_loc < n ? k_loc : n;
-    for (int t = 0; t < take; ++t) keep[idx[t]] = 1;
+    for (int t = 0; t < take; ++t) keep[c[t].slot] = 1;
     nloc += take;
   }
   if (nloc > kt) {
-    free(idx);
+    free(c);
     free(s);
     return -1;
   }
   int n = 0;
   for (int i = 0; i < nc; ++i)
-    if (!keep[i]) idx[n++] = i;
-  qsort(idx, (size_t)n, sizeof(int), cmp_slot_by_key_desc);
-  for (int t = 0; t < kt - nloc && t < n; ++t) keep[idx[t]] = 1;
+    if (!keep[i]) {
+      c[n].s = s[i];
+      c[n].slot = i;
+      ++n;
+    }
+  qsort(c, (size_t)n, sizeof(orc_cand), cmp_cand_desc);
+  for (int t = 0; t < kt - nloc && t < n; ++t) keep[c[t].slot] = 1;
   for (int i = nc; i < N; ++i) keep[i] = 1;
-  free(idx);
+  free(c);
   free(s);
   return 0;
 }
