@@ -108,6 +108,10 @@ class Workload:
     steps: int                    # EMA steps in the query stream
     short_steps: int              # trailing steps that follow u_short
     meta: dict = field(default_factory=dict)
+    # optional schedule of the query stream: (first step, kind) pairs in
+    # increasing order, kind in {"long", "short", "diffuse"}; when set it
+    # replaces the long-then-short default
+    phases: tuple = ()
 
     @property
     def B(self) -> int:
@@ -119,11 +123,17 @@ class Workload:
         s = self.shape
         G = s.Hq // s.Hkv
         g = _gen(self.device, self.seed * 7919 + 1000003 * (t + 1))
-        use_short = t >= self.steps - self.short_steps
-        u = self.u_short if use_short else self.u_long
+        if self.phases:
+            kind = [k for t0, k in self.phases if t0 <= t][-1]
+        else:
+            kind = "short" if t >= self.steps - self.short_steps else "long"
+        u = self.u_short if kind == "short" else self.u_long
         base = u.repeat_interleave(G, dim=2)  # [B][L][Hq][d]
         noise = torch.randn(base.shape, generator=g, device=self.device, dtype=torch.float32)
-        q = 0.8 * math.sqrt(s.d) * base + 0.6 * noise
+        if kind == "diffuse":
+            q = noise  # no preferred direction, RMS 1
+        else:
+            q = 0.8 * math.sqrt(s.d) * base + 0.6 * noise
         if s.qnorm:
             q = rms_norm_heads(q)
         return q.contiguous()
@@ -131,12 +141,34 @@ class Workload:
     def first_step(self, t: int) -> torch.Tensor:
         return torch.full((self.B,), 1 if t == 0 else 0, dtype=torch.uint8, device=self.device)
 
+    def new_tokens(self, event: int, n: int):
+        """Keys and values of the n tokens decoded after boundary event
+        `event` (0-based), for every request: bf16 N(0, 1), [B][L][Hkv][n][d]
+        each.  Seeded per event, independent of what the event did."""
+        s = self.shape
+        g = _gen(self.device, self.seed * 104729 + 7919 * (event + 1) + 17)
+        shp = (self.B, s.L, s.Hkv, n, s.d)
+        k = torch.randn(shp, generator=g, device=self.device, dtype=torch.float32)
+        v = torch.randn(shp, generator=g, device=self.device, dtype=torch.float32)
+        return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+    def write_tokens(self, r: int, slot0: int, k: torch.Tensor, v: torch.Tensor):
+        """Store [L][Hkv][n][d] keys/values of request r at logical slots
+        slot0 .. slot0 + n - 1 (within one page) through its block table."""
+        b = self.shape.b
+        n = k.shape[2]
+        assert slot0 % b + n <= b, "appended tokens must stay in one page"
+        page = int(self.block_table[r, slot0 // b].item())
+        o = slot0 % b
+        self.k_pool[:, page, :, o:o + n] = k
+        self.v_pool[:, page, :, o:o + n] = v
+
 
 def make_workload(shape: ModelShape, pages_per_request, pool_pages: int, *, seed: int,
                   device, align=None, cluster_sizes=None, cluster_scale: float = 2.0,
                   free_pages: int = 0, max_pages: int | None = None, steps: int = 1024,
                   short_steps: int = 32, max_slots: int = 512, max_pos: int | None = None,
-                  value_pool: bool = True) -> Workload:
+                  value_pool: bool = True, phases: tuple = ()) -> Workload:
     """Build one scenario.
 
     pages_per_request: list of P_r (N_r = P_r * b at the boundary).
@@ -224,7 +256,7 @@ def make_workload(shape: ModelShape, pages_per_request, pool_pages: int, *, seed
         free_stack=torch.from_numpy(free_stack).to(device),
         free_count=torch.tensor([free_pages], **i32), rope=rope,
         u_short=u_s, u_long=u_l, max_slots=max_slots, seed=seed, steps=steps,
-        short_steps=short_steps, meta=dict(align=list(align)))
+        short_steps=short_steps, meta=dict(align=list(align)), phases=tuple(phases))
 
 
 def tiny(variant: str, device="cpu") -> Workload:
@@ -271,3 +303,45 @@ def batch64(device="cuda", pool_pages: int = 6144, seed: int = SEED_BASE + 3,
     return make_workload(LLAMA8B, P.tolist(), pool_pages, seed=seed, device=device, align=align,
                          cluster_sizes=sizes, free_pages=free, max_pages=136, steps=256,
                          short_steps=32, value_pool=value_pool)
+
+
+EVENT_GAP = 256  # decoded tokens (and summary updates) between two boundary events
+
+
+def qwen16k_phase(device="cuda", events: int = 10, shape: ModelShape = QWEN3_8B,
+                  warmup: int = 1024) -> Workload:
+    """Qwen3-8B shape (36 layers, 32 Q / 8 KV heads, query RMSNorm), one
+    request of 16384 tokens = 64 pages in a 96-page pool with 16 free pages,
+    `events` boundary events EVENT_GAP decoding steps apart.  Per-row clusters
+    (log-uniform sizes in [50, 4000]) follow u_L.  Query stream: diffuse for
+    `warmup` steps, concentrated on u_L over the first half of the events,
+    diffuse again over the second half, so that the short summary first leads
+    the long one onto the clusters (Delta < 0) and then leaves them
+    (Delta > 0).  Event e (0-based) takes the query of step
+    warmup + EVENT_GAP * (e + 1) - 1 as its current query."""
+    seed = SEED_BASE + 2
+    rng = np.random.default_rng(seed)
+    sizes = _log_uniform_sizes(rng, (shape.L, shape.Hkv))
+    half = events // 2
+    phases = ((0, "diffuse"), (warmup, "long"), (warmup + EVENT_GAP * half, "diffuse"))
+    steps = warmup + EVENT_GAP * events
+    return make_workload(shape, [64], 96, seed=seed, device=device, align=["L"],
+                         cluster_sizes=[sizes], free_pages=16, max_pages=80, steps=steps,
+                         max_slots=4, max_pos=16384 + EVENT_GAP * (events + 1) + 16,
+                         phases=phases)
+
+
+def qwen32k_stress(device="cuda", batch: int = 16, shape: ModelShape = QWEN3_8B,
+                   warmup: int = 512, events: int = 8) -> Workload:
+    """Qwen3-8B shape, `batch` requests of 32768 tokens = 128 pages each, the
+    pool exactly their pages (no free page: every Grow falls back), per-row
+    log-uniform clusters on u_S or u_L by request, `events` successive
+    boundary events EVENT_GAP steps apart after a `warmup`-step stream."""
+    seed = SEED_BASE + 4
+    rng = np.random.default_rng(seed)
+    align = [str(a) for a in rng.choice(["S", "L"], size=batch)]
+    sizes = [_log_uniform_sizes(rng, (shape.L, shape.Hkv)) for _ in range(batch)]
+    return make_workload(shape, [128] * batch, 128 * batch, seed=seed, device=device,
+                         align=align, cluster_sizes=sizes, free_pages=0, max_pages=128,
+                         steps=warmup + EVENT_GAP * events, max_slots=batch,
+                         max_pos=32768 + EVENT_GAP * (events + 1) + 16)

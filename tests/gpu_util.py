@@ -31,9 +31,14 @@ def bf16_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def runner_for(wl, cfg: gb.Config, want_abar=True, want_dropped=True) -> BoundaryRunner:
+def runner_for(wl, cfg: gb.Config, want_abar=True, want_dropped=True,
+               qstate: torch.Tensor | None = None) -> BoundaryRunner:
+    """A runner over the workload's current batch state (page counts read
+    back from the device); qstate is reused when given."""
     s = wl.shape
-    qstate = torch.zeros((s.L, wl.max_slots, 2, s.Hq, s.d), dtype=torch.float32, device=wl.device)
+    if qstate is None:
+        qstate = torch.zeros((s.L, wl.max_slots, 2, s.Hq, s.d), dtype=torch.float32,
+                             device=wl.device)
     pool = gb.Pool(wl.k_pool, wl.v_pool, wl.free_stack, wl.free_count)
     batch = gb.Batch(wl.block_table, wl.num_pages, wl.num_tokens, wl.slot, wl.position,
                      wl.num_pages.cpu().numpy().astype(np.int32).copy())
