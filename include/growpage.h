@@ -37,7 +37,8 @@
  *  - Rotary table: [rope_rows][d] fp32; row p holds cos(p * f_j) for the d/2
  *    frequencies f_j, then sin(p * f_j) (rotate-half pairing (j, j + d/2)).
  *
- * Version 1 limits: d = 128, b = 256, Hq / Hkv = 4, batch <= 1024.
+ * Version 1 limits: d = 128, b = 256, Hq / Hkv = 4, batch <= 1024, at most
+ * 2^23 cached tokens (32768 pages) per request.
  */
 #ifndef GROWPAGE_H
 #define GROWPAGE_H

@@ -171,6 +171,7 @@ gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const fl
   const int B = bt->batch;
   const int64_t total_tokens = total_pages * c->p.b;
   const int64_t max_tokens = max_pages_used * c->p.b;
+  if (max_tokens > gp::kMaxRequestTokens) return GP_ERR_UNSUPPORTED;
   const gp::WsLayout w = gp::ws_layout(c->p, B, total_tokens, max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   if (!ws || ws_bytes < w.total) return GP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

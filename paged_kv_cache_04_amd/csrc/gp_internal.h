@@ -17,6 +17,9 @@ constexpr int kPage = 256;
 constexpr int kGroup = 4;
 constexpr int kNQ = 2 * kGroup;
 constexpr int kMaxBatch = 1024;
+// Longest request gp_demand accepts: the demand kernel's per-lane fp64 sums
+// of 2^-40 masses stay exact up to 2^13 terms per lane of a 1024-thread block.
+constexpr int64_t kMaxRequestTokens = int64_t(1) << 23;
 // Demand kernel: persistent workgroups per CU (each holds one row at a time).
 #ifndef GP_DEMAND_BLOCKS_PER_CU
 #define GP_DEMAND_BLOCKS_PER_CU 1

@@ -44,7 +44,7 @@ constexpr int kWaveStage = 64 * kHalfPad;     // bytes per wave
 constexpr int kLdsBytes = kDW * kWaveStage;   // 147456, reused after scoring
 constexpr int kH1 = 2048;                     // first-digit buckets
 constexpr int kH2 = 1024;                     // second/third-digit buckets
-constexpr int kListCap = (kLdsBytes - 2 * kH1 * 12 - kH2 * 12) / 4;  // boundary members in LDS
+constexpr int kListCap = (kLdsBytes - 2 * kH1 * 8 - kH2 * 12) / 4;  // boundary members in LDS
 
 // acc[qi] += q[qi][e] * k[e] for e = 0..3 in order (4 bf16 keys in k).
 __device__ __forceinline__ void fma_quad(float* acc, const float* q, u32x2 k) {
@@ -134,6 +134,66 @@ __device__ __forceinline__ void scan_desc(const uint32_t* cnt, const uint64_t* m
   c_above = __shfl(best_c, hl);
 }
 
+__device__ __forceinline__ float uniform_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// floor(v * 2^40) as an integer-valued float: exact, since below 2^23 floorf
+// is exact and from 2^23 on every fp32 value is an integer (v <= 1).
+__device__ __forceinline__ float mass40(float v) { return __builtin_floorf(v * kFix); }
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ void load_logits8(const float* lg, int64_t i, float (&lv)[kNQ]) {
+  const float4* lp = reinterpret_cast<const float4*>(lg + i * kNQ);
+  const float4 x0 = lp[0], x1 = lp[1];
+  lv[0] = x0.x; lv[1] = x0.y; lv[2] = x0.z; lv[3] = x0.w;
+  lv[4] = x1.x; lv[5] = x1.y; lv[6] = x1.z; lv[7] = x1.w;
+}
+
+// Wave 0, first radix digit: over kH1 bucket masses (integer-valued fp64,
+// exact), the largest bucket d with p_den * (mass of buckets >= d) >= target;
+// m_above returns the mass of the buckets above d.
+__device__ __forceinline__ void scan_first_digit(const double* mass, uint64_t target,
+                                                 uint32_t p_den, uint64_t& m_above, int& d_out) {
+  constexpr int PER = kH1 / 64;
+  const int lane = threadIdx.x & 63;
+  uint64_t mv[PER];
+  uint64_t lm = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    mv[u] = (uint64_t)mass[lane * PER + u];
+    lm += mv[u];
+  }
+  uint64_t sm = lm;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t vm = shfl_down_u64(sm, off);
+    if (lane + off < 64) sm += vm;
+  }
+  uint64_t cum = sm - lm;  // mass of the buckets of higher lanes
+  int best = -1;
+  uint64_t best_m = 0;
+#pragma unroll
+  for (int u = PER - 1; u >= 0; --u) {
+    const uint64_t before = cum;
+    cum += mv[u];
+    if (best < 0 && cum * (uint64_t)p_den >= target) {
+      best = lane * PER + u;
+      best_m = before;
+    }
+  }
+  const unsigned long long ok = __ballot(best >= 0);
+  const int hl = 63 - __clzll(ok);
+  d_out = __shfl(best, hl);
+  const unsigned lo = __shfl((unsigned)best_m, hl), hi = __shfl((unsigned)(best_m >> 32), hl);
+  m_above = ((uint64_t)hi << 32) | lo;
+}
+
 struct DemandArgs {
   const uint16_t* k_pool;
   int pool_pages;
@@ -167,7 +227,7 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
   __shared__ int s_list_n;
   __shared__ int s_dig;
   __shared__ uint64_t s_mab;
-  __shared__ uint32_t s_cab;
+  __shared__ uint32_t s_cab;  // slots above the boundary so far
   if (!a.hdr->valid) return;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -177,11 +237,10 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
   float* rk = a.ring_keys + (int64_t)blockIdx.x * a.ring_tokens * 2;
   unsigned char* my = lds + w * kWaveStage;
   // LDS views used after scoring
-  uint32_t* h1c = reinterpret_cast<uint32_t*>(lds);             // [2][kH1]
-  uint64_t* h1m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 4);  // [2][kH1]
-  uint32_t* h2c = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 12);  // [kH2]
-  uint64_t* h2m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 12 + kH2 * 4);  // [kH2]
-  uint32_t* list = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 12 + kH2 * 12);  // [kListCap]
+  double* h1m = reinterpret_cast<double*>(lds);                              // [2][kH1]
+  uint32_t* h2c = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 8);            // [kH2]
+  uint64_t* h2m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 8 + kH2 * 4);  // [kH2]
+  uint32_t* list = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 8 + kH2 * 12);  // [kListCap]
 
   while (true) {
     if (t == 0) s_item = atomicAdd(a.row_counter, 1);
@@ -318,41 +377,49 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
       s_m[1][t] = fmaxf(d, e);
     }
     // clear the first-digit histograms (the stage is free now)
-    for (int k = t; k < 2 * kH1; k += kDT) {
-      h1c[k] = 0;
-      h1m[k] = 0;
-    }
+    for (int k = t; k < 2 * kH1; k += kDT) h1m[k] = 0.0;
     __syncthreads();
     float mdem[kNQ], mall[kNQ];
     bool same[kNQ];
 #pragma unroll
-    for (int q = 0; q < kNQ; ++q) {
-      mdem[q] = s_m[0][q];
-      mall[q] = s_m[1][q];
+    for (int q = 0; q < kNQ; ++q) {  // block-uniform: held in scalar registers
+      mdem[q] = uniform_f(s_m[0][q]);
+      mall[q] = uniform_f(s_m[1][q]);
       same[q] = mdem[q] == mall[q];
     }
 
     // ---- 2. exact fixed-point normalisers ----------------------------------------
+    // Z = sum over the set of floor(e * 2^40).  Each term is an integer-valued
+    // float (mass40); a lane sums its ceil(N / kDT) terms in fp64, exactly
+    // while that is below 2^13 terms; lanes and waves combine in uint64.
+    // Z over all slots = (sum over C_t) + (sum over the newest page); when the
+    // two maxima agree the C_t part is also Z over C_t.
     {
-      uint64_t zd[kNQ], za[kNQ];
+      double zc[kNQ], zd[kNQ];
 #pragma unroll
-      for (int q = 0; q < kNQ; ++q) zd[q] = za[q] = 0;
-      for (int64_t i = t; i < N; i += kDT) {
-        const float4* lp = reinterpret_cast<const float4*>(lg + i * kNQ);
-        const float4 x0 = lp[0], x1 = lp[1];
-        const float lv[kNQ] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        const bool dem = i < ndem;
+      for (int q = 0; q < kNQ; ++q) zc[q] = zd[q] = 0.0;
+      for (int64_t i = t; i < ndem; i += kDT) {
+        float lv[kNQ];
+        load_logits8(lg, i, lv);
 #pragma unroll
         for (int q = 0; q < kNQ; ++q) {
-          const float ea = gp_exp(lv[q] - mall[q]);
-          za[q] += fix40(ea);
-          if (dem) zd[q] += fix40(same[q] ? ea : gp_exp(lv[q] - mdem[q]));
+          zc[q] += (double)mass40(gp_exp(lv[q] - mall[q]));
+          if (!same[q]) zd[q] += (double)mass40(gp_exp(lv[q] - mdem[q]));
         }
       }
 #pragma unroll
+      for (int q = 0; q < kNQ; ++q)
+        if (same[q]) zd[q] = zc[q];
+      for (int64_t i = ndem + t; i < N; i += kDT) {
+        float lv[kNQ];
+        load_logits8(lg, i, lv);
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) zc[q] += (double)mass40(gp_exp(lv[q] - mall[q]));
+      }
+#pragma unroll
       for (int v = 0; v < 2 * kNQ; ++v) {
-        const uint64_t s = wave_sum_u64(v < kNQ ? zd[v] : za[v - kNQ]);
-        if (lane == 0) s_red[w][v] = s;
+        const uint64_t sv = wave_sum_u64((uint64_t)(v < kNQ ? zd[v] : zc[v - kNQ]));
+        if (lane == 0) s_red[w][v] = sv;
       }
       __syncthreads();
       if (t < 2 * kNQ) {
@@ -370,15 +437,13 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
       float rd[kNQ], ra[kNQ];
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) {
-        rd[q] = s_rho[0][q];
-        ra[q] = s_rho[1][q];
+        rd[q] = uniform_f(s_rho[0][q]);
+        ra[q] = uniform_f(s_rho[1][q]);
       }
-      uint64_t ws0 = 0, ws1 = 0;
-      for (int64_t i = t; i < N; i += kDT) {
-        const float4* lp = reinterpret_cast<const float4*>(lg + i * kNQ);
-        const float4 x0 = lp[0], x1 = lp[1];
-        const float lv[kNQ] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        const bool dem = i < ndem;
+      double w0 = 0.0, w1 = 0.0;
+      for (int64_t i = t; i < ndem; i += kDT) {
+        float lv[kNQ];
+        load_logits8(lg, i, lv);
         float aa[2], ad[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -388,40 +453,48 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
             const int q = x * kGroup + g;
             const float ea = gp_exp(lv[q] - mall[q]);
             sa = sa + ea * ra[q];
-            if (dem) {
-              const float ed = same[q] ? ea : gp_exp(lv[q] - mdem[q]);
-              sd = sd + ed * rd[q];
-            }
+            const float ed = same[q] ? ea : gp_exp(lv[q] - mdem[q]);
+            sd = sd + ed * rd[q];
           }
-          aa[x] = sa / (float)kGroup;
-          ad[x] = sd / (float)kGroup;
+          aa[x] = sa * (1.0f / (float)kGroup);
+          ad[x] = sd * (1.0f / (float)kGroup);
         }
         a.imp[row_tok + i] = fmaxf(aa[0], aa[1]);
         if (a.abar) reinterpret_cast<float2*>(a.abar)[row_tok + i] = make_float2(aa[0], aa[1]);
-        if (dem) {
-          reinterpret_cast<float2*>(rk)[i] = make_float2(ad[0], ad[1]);
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const uint32_t key = __float_as_uint(ad[x]);
-            const uint64_t wm = fix40(ad[x]);
-            atomicAdd(&h1c[x * kH1 + (key >> 20)], 1u);
-            atomicAdd((unsigned long long*)&h1m[x * kH1 + (key >> 20)], (unsigned long long)wm);
-          }
-          ws0 += fix40(ad[0]);
-          ws1 += fix40(ad[1]);
-        }
+        reinterpret_cast<float2*>(rk)[i] = make_float2(ad[0], ad[1]);
+        const float f0 = mass40(ad[0]), f1 = mass40(ad[1]);
+        atomicAdd(&h1m[__float_as_uint(ad[0]) >> 20], (double)f0);
+        atomicAdd(&h1m[kH1 + (__float_as_uint(ad[1]) >> 20)], (double)f1);
+        w0 += (double)f0;
+        w1 += (double)f1;
       }
-      ws0 = wave_sum_u64(ws0);
-      ws1 = wave_sum_u64(ws1);
+      for (int64_t i = ndem + t; i < N; i += kDT) {
+        float lv[kNQ];
+        load_logits8(lg, i, lv);
+        float aa[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          float sa = 0.0f;
+#pragma unroll
+          for (int g = 0; g < kGroup; ++g) {
+            const int q = x * kGroup + g;
+            sa = sa + gp_exp(lv[q] - mall[q]) * ra[q];
+          }
+          aa[x] = sa * (1.0f / (float)kGroup);
+        }
+        a.imp[row_tok + i] = fmaxf(aa[0], aa[1]);
+        if (a.abar) reinterpret_cast<float2*>(a.abar)[row_tok + i] = make_float2(aa[0], aa[1]);
+      }
+      const uint64_t ws0 = wave_sum_u64((uint64_t)w0), ws1 = wave_sum_u64((uint64_t)w1);
       if (lane == 0) {
         s_red[w][0] = ws0;
         s_red[w][1] = ws1;
       }
       __syncthreads();
       if (t < 2) {
-        uint64_t s = 0;
-        for (int ww = 0; ww < kDW; ++ww) s += s_red[ww][t];
-        s_W[t] = s;
+        uint64_t sw = 0;
+        for (int ww = 0; ww < kDW; ++ww) sw += s_red[ww][t];
+        s_W[t] = sw;
       }
       __syncthreads();
     }
@@ -436,28 +509,36 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
       const uint64_t target = s_W[x] * (uint64_t)a.p_num;
       if (w == 0) {
         uint64_t mab = 0;
-        uint32_t cab = 0;
         int d1;
-        scan_desc<kH1>(h1c + x * kH1, h1m + x * kH1, target, (uint32_t)a.p_den, mab, cab, d1);
+        scan_first_digit(h1m + x * kH1, target, (uint32_t)a.p_den, mab, d1);
         if (lane == 0) {
           s_dig = d1;
           s_mab = mab;
-          s_cab = cab;
+          s_cab = 0;
           s_list_n = 0;
         }
       }
       __syncthreads();
       const uint32_t d1 = (uint32_t)s_dig;
-      const uint32_t cnt1 = h1c[x * kH1 + d1];
       uint32_t prefix = d1 << 20;
-      const bool in_lds = cnt1 <= (uint32_t)kListCap;
-      if (in_lds) {
+      // members of the boundary bucket into LDS (as many as fit), and the
+      // number of slots in buckets above it
+      {
+        uint32_t above = 0;
         for (int64_t i = t; i < ndem; i += kDT) {
           const uint32_t key = __float_as_uint(rk[i * 2 + x]);
-          if ((key >> 20) == d1) list[atomicAdd(&s_list_n, 1)] = key;
+          const uint32_t dig = key >> 20;
+          above += dig > d1;
+          if (dig == d1) {
+            const int idx = atomicAdd(&s_list_n, 1);
+            if (idx < kListCap) list[idx] = key;
+          }
         }
+        above = wave_sum_u32(above);
+        if (lane == 0) atomicAdd(&s_cab, above);
       }
       __syncthreads();
+      const bool in_lds = s_list_n <= kListCap;
       // digits 2 (bits 19..10) and 3 (bits 9..0)
       for (int pass = 0; pass < 2; ++pass) {
         const int shift = pass == 0 ? 10 : 0;

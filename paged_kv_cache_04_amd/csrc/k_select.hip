@@ -6,15 +6,16 @@
 // Candidates C = [0, N - R): the R newest slots are always kept.  Order:
 // larger importance first, equal importance the newer slot first.  With
 // exactly b candidates to drop per row, the selection is computed from the
-// bottom:
-//   step 1: each logical page (block) protects its top-min(k_loc, |B_j|)
-//           candidates (one wave per block, 4 keys per lane, bit-serial
-//           threshold search with ballots; ties broken by slot);
-//   step 2: among the unprotected candidates, a 4-pass 8-bit radix select
-//           finds the importance value v of the b-th smallest;
-//   step 3: candidates below v are dropped, and of those equal to v the
-//           oldest ones until exactly b are dropped (block-wide prefix count
-//           in slot order); the dropped slots are written in ascending order.
+// bottom, on the row held in LDS when it fits (read from HBM once):
+//   1. the b smallest candidates of C: a 3-digit radix select (11 + 10 + 10
+//      bits) finds the value v of the b-th smallest; candidates below v are
+//      dropped and of those equal to v the oldest until exactly b (block-wide
+//      prefix count in slot order); dropped slots written in ascending order;
+//   2. if no block loses more than |B_j| - min(k_loc, |B_j|) candidates, no
+//      protected (block top-k_loc) candidate was dropped and this is Eq. 10's
+//      answer; otherwise each block's top-min(k_loc, |B_j|) is marked (one
+//      wave per block, bit-serial threshold search with ballots, ties by
+//      slot) and step 1 is repeated over the unmarked candidates.
 // Importance values are non-negative fp32, so their bit patterns order like
 // the values.
 #include "gp_internal.h"
@@ -23,6 +24,9 @@ namespace gp {
 
 constexpr int kSel = 1024;
 constexpr int kMaxRowTokens = 65536;
+constexpr int kSelLdsTokens = 32768;  // candidates held in LDS (128 KiB)
+constexpr int kSelH1 = 2048;          // first radix digit: bits 30..20
+constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
 
 // Exclusive prefix sum over the block (1024 threads); total in *total.
 __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
@@ -51,33 +55,115 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
   return base + x - v;
 }
 
-__global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, int kloc,
-                                                 const WsHeader* __restrict__ hdr,
-                                                 const int64_t* __restrict__ page_off,
-                                                 const int8_t* __restrict__ action,
-                                                 const float* __restrict__ imp,
-                                                 int32_t* __restrict__ dropped,
-                                                 int32_t* __restrict__ dropped_out,
-                                                 int32_t* __restrict__ err) {
-  __shared__ uint32_t sloc[kMaxRowTokens / 32];
-  __shared__ uint32_t hcnt[256];
-  __shared__ int scanbuf[kSel / 64];
-  __shared__ uint32_t s_prefix, s_below;
-  if (!hdr->valid) return;
-  const int LH = L * Hkv;
-  const int row = blockIdx.x;
-  const int r = row / LH, lh = row % LH;
-  if (action && action[r] != GP_COMPRESS) return;
-  const int64_t P = page_off[r + 1] - page_off[r];
+// Steps 2-3: the b smallest candidates of [0, nc) (skipping those marked in
+// the S_loc bitmap when PROT), written ascending to dst (and dst2); without
+// PROT each dropped slot is also counted in blkcnt[its block].  Returns the
+// number of candidates the threshold selects (b unless the row is too short).
+template <bool PROT>
+__device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc, int b,
+                                             const uint32_t* sloc, uint32_t* hcnt, int* scanbuf,
+                                             uint32_t& s_prefix, uint32_t& s_below,
+                                             int32_t* dst, int32_t* dst2, int* blkcnt) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  if (P < 2) {
-    if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
-    return;
+  // step 2: value of the b-th smallest unprotected candidate.  Three radix
+  // digits: bits 30..20 (the exponent and three mantissa bits, so that the
+  // buckets spread the values and the counting atomics rarely collide), then
+  // bits 19..10 and 9..0.  The sign bit is 0 for every importance value.
+  uint32_t prefix = 0, mask = 0, below = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 0 ? kSelH1 : kSelH2;
+    for (int k = t; k < nb; k += kSel) hcnt[k] = 0;
+    __syncthreads();
+    for (int i = t; i < nc; i += kSel) {
+      if (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) continue;
+      const uint32_t key = __float_as_uint(s[i]);
+      if ((key & mask) == prefix) atomicAdd(&hcnt[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      // ascending scan: the bucket where the count of smaller values reaches b
+      const int per = nb / 64;
+      uint32_t lc = 0;
+      for (int u = 0; u < per; ++u) lc += hcnt[per * lane + u];
+      uint32_t incl = lc;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      uint32_t cum = below + incl - lc;
+      int best = -1;
+      uint32_t best_below = 0;
+      for (int u = 0; u < per; ++u) {
+        const uint32_t before = cum;
+        cum += hcnt[per * lane + u];
+        if (best < 0 && cum >= (uint32_t)b) {
+          best = per * lane + u;
+          best_below = before;
+        }
+      }
+      const unsigned long long ok = __ballot(best >= 0);
+      const int ll = __ffsll((long long)ok) - 1;
+      if (lane == ll) {
+        s_prefix = prefix | ((uint32_t)best << shift);
+        s_below = best_below;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    below = s_below;
+    mask |= (uint32_t)(nb - 1) << shift;
+    __syncthreads();
   }
-  const int N = (int)(P * b), nc = N - R;
-  const int64_t row_tok = (int64_t)LH * page_off[r] * b + (int64_t)lh * N;
-  const float* __restrict__ s = imp + row_tok;
+  const uint32_t v = prefix;
+  const int need = b - (int)below;
 
+  // step 3: ties at v go oldest first; write dropped slots in ascending order
+  const int q = (nc + kSel - 1) / kSel;
+  const int lo = t * q < nc ? t * q : nc;
+  const int hi = lo + q < nc ? lo + q : nc;
+  int ties = 0;
+  for (int i = lo; i < hi; ++i)
+    if (!(PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) && __float_as_uint(s[i]) == v) ++ties;
+  int total;
+  const int tie0 = block_excl_scan(ties, scanbuf, &total);
+  int nd = 0;
+  {
+    int tr = tie0;
+    for (int i = lo; i < hi; ++i) {
+      if (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) continue;
+      const uint32_t key = __float_as_uint(s[i]);
+      if (key < v) ++nd;
+      else if (key == v) nd += (tr++ < need);
+    }
+  }
+  const int pos0 = block_excl_scan(nd, scanbuf, &total);
+  {
+    int tr = tie0, pos = pos0;
+    for (int i = lo; i < hi; ++i) {
+      if (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) continue;
+      const uint32_t key = __float_as_uint(s[i]);
+      bool drop = key < v;
+      if (key == v) drop = tr++ < need;
+      if (drop) {
+        if (pos < b) {
+          dst[pos] = i;
+          if (dst2) dst2[pos] = i;
+          if (!PROT) atomicAdd(&blkcnt[i >> 8], 1);
+        }
+        ++pos;
+      }
+    }
+  }
+  return total;
+}
+
+// Step 1: S_loc of every block as a bitmap.
+__device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int P, int nc,
+                                               int kloc, uint32_t* sloc) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  (void)t;
   // step 1: per-block quota S_loc as a bitmap
   for (int j = wv; j < P; j += kSel / 64) {
     const int blk = j * kPage;
@@ -129,96 +215,84 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   }
   __syncthreads();
 
-  // step 2: value of the b-th smallest unprotected candidate
-  uint32_t prefix = 0, mask = 0, below = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int k = t; k < 256; k += kSel) hcnt[k] = 0;
-    __syncthreads();
-    for (int i = t; i < nc; i += kSel) {
-      if ((sloc[i >> 5] >> (i & 31)) & 1u) continue;
-      const uint32_t key = __float_as_uint(s[i]);
-      if ((key & mask) == prefix) atomicAdd(&hcnt[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wv == 0) {
-      uint32_t c[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) c[u] = hcnt[4 * lane + u];
-      const uint32_t lc = c[0] + c[1] + c[2] + c[3];
-      uint32_t incl = lc;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      uint32_t cum = below + incl - lc;
-      int best = -1;
-      uint32_t best_below = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t before = cum;
-        cum += c[u];
-        if (best < 0 && cum >= (uint32_t)b) {
-          best = 4 * lane + u;
-          best_below = before;
-        }
-      }
-      const unsigned long long ok = __ballot(best >= 0);
-      const int ll = __ffsll((long long)ok) - 1;
-      if (lane == ll) {
-        s_prefix = prefix | ((uint32_t)best << shift);
-        s_below = best_below;
-      }
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    below = s_below;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const uint32_t v = prefix;
-  const int need = b - (int)below;
+}
 
-  // step 3: ties at v go oldest first; write dropped slots in ascending order
-  const int q = (nc + kSel - 1) / kSel;
-  const int lo = t * q < nc ? t * q : nc;
-  const int hi = lo + q < nc ? lo + q : nc;
-  int ties = 0;
-  for (int i = lo; i < hi; ++i)
-    if (!((sloc[i >> 5] >> (i & 31)) & 1u) && __float_as_uint(s[i]) == v) ++ties;
-  int total;
-  const int tie0 = block_excl_scan(ties, scanbuf, &total);
-  int nd = 0;
-  {
-    int tr = tie0;
-    for (int i = lo; i < hi; ++i) {
-      if ((sloc[i >> 5] >> (i & 31)) & 1u) continue;
-      const uint32_t key = __float_as_uint(s[i]);
-      if (key < v) ++nd;
-      else if (key == v) nd += (tr++ < need);
+// One row whose importance values are at s (LDS or global memory).  The
+// b smallest candidates are found first without the block quotas; they are
+// the answer unless some block would lose more than |B_j| - min(k_loc,
+// |B_j|) of its candidates (then one of them is in that block's protected
+// top), in which case the quotas are computed and the selection repeated
+// over the unprotected candidates.  (The b smallest of C avoid S_loc, so
+// they are also the b smallest of C minus S_loc.)
+__device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int b,
+                                           int kloc, uint32_t* sloc, uint32_t* hcnt,
+                                           int* scanbuf, int* blkcnt, uint32_t& s_prefix,
+                                           uint32_t& s_below, int32_t* dst, int32_t* dst2,
+                                           int32_t* err) {
+  const int t = threadIdx.x;
+  for (int j = t; j < P; j += kSel) blkcnt[j] = 0;
+  __syncthreads();
+  int total = drop_smallest<false>(s, nc, b, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
+                                   blkcnt);
+  __syncthreads();
+  int over = 0;
+  if (kloc > 0)
+    for (int j = t; j < P; j += kSel) {
+      const int nb = nc - j * kPage < kPage ? nc - j * kPage : kPage;
+      const int keep_min = kloc < nb ? kloc : nb;
+      over |= blkcnt[j] > nb - keep_min;
     }
-  }
-  const int pos0 = block_excl_scan(nd, scanbuf, &total);
-  int32_t* dst = dropped + (int64_t)row * b;
-  int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * b : nullptr;
-  {
-    int tr = tie0, pos = pos0;
-    for (int i = lo; i < hi; ++i) {
-      if ((sloc[i >> 5] >> (i & 31)) & 1u) continue;
-      const uint32_t key = __float_as_uint(s[i]);
-      bool drop = key < v;
-      if (key == v) drop = tr++ < need;
-      if (drop) {
-        if (pos < b) {
-          dst[pos] = i;
-          if (dst2) dst2[pos] = i;
-        }
-        ++pos;
-      }
-    }
+  if (__syncthreads_or(over)) {
+    protect_blocks(s, P, nc, kloc, sloc);
+    __syncthreads();
+    total = drop_smallest<true>(s, nc, b, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
+                                nullptr);
   }
   if (t == 0 && total != b) atomicOr(err, GP_DEVERR_SHORT);
+}
+
+__global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, int kloc,
+                                                 const WsHeader* __restrict__ hdr,
+                                                 const int64_t* __restrict__ page_off,
+                                                 const int8_t* __restrict__ action,
+                                                 const float* __restrict__ imp,
+                                                 int32_t* __restrict__ dropped,
+                                                 int32_t* __restrict__ dropped_out,
+                                                 int32_t* __restrict__ err) {
+  __shared__ __attribute__((aligned(16))) float srow[kSelLdsTokens];
+  __shared__ uint32_t sloc[kMaxRowTokens / 32];
+  __shared__ uint32_t hcnt[kSelH1];
+  __shared__ int scanbuf[kSel / 64];
+  __shared__ int blkcnt[kMaxRowTokens / kPage];
+  __shared__ uint32_t s_prefix, s_below;
+  if (!hdr->valid) return;
+  const int LH = L * Hkv;
+  const int row = blockIdx.x;
+  const int r = row / LH, lh = row % LH;
+  if (action && action[r] != GP_COMPRESS) return;
+  const int64_t P = page_off[r + 1] - page_off[r];
+  const int t = threadIdx.x;
+  if (P < 2) {
+    if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
+    return;
+  }
+  const int N = (int)(P * b), nc = N - R;
+  const int64_t row_tok = (int64_t)LH * page_off[r] * b + (int64_t)lh * N;
+  const float* __restrict__ s = imp + row_tok;
+  int32_t* dst = dropped + (int64_t)row * b;
+  int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * b : nullptr;
+  if (nc <= kSelLdsTokens) {
+    // the row's candidates are read from HBM once, every pass runs on LDS
+    const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
+    for (int i = t; i < n4; i += kSel)
+      reinterpret_cast<float4*>(srow)[i] = reinterpret_cast<const float4*>(s)[i];
+    __syncthreads();
+    select_row(srow, (int)P, nc, b, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
+               dst2, err);
+  } else {
+    select_row(s, (int)P, nc, b, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst, dst2,
+               err);
+  }
 }
 
 hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t* action,

@@ -88,6 +88,35 @@ def test_constant_keys_all_ties():
 
 
 @needs_gpu
+def test_junk_page_needs_block_quota():
+    """One logical page of request 0 holds keys pointing away from both
+    summary directions in every (layer, KV head): their attention underflows
+    to 0, so the 256 least important candidates of each row all lie in that
+    page.  Eq. 10's block quota keeps its 64 newest (ties, newer first) and
+    the other 192 drops come from the rest of the row, which the selection
+    reaches only after marking the block quotas."""
+    log("test_junk_page_needs_block_quota")
+    wl = synth.make_workload(SMALL, [6, 5], 24, seed=321, device="cuda", align=["L", "S"],
+                             cluster_sizes=[40, 40], free_pages=0, steps=120, short_steps=16,
+                             max_slots=4)
+    s = wl.shape
+    half = s.d // 2
+    pos = int(wl.position[0].item())
+    cos, sin = wl.rope[pos, :half], wl.rope[pos, half:]
+    away = synth.rotate_keys(-100.0 * (wl.u_short[0] + wl.u_long[0]), cos, sin)  # [L][Hkv][d]
+    page = int(wl.block_table[0, 2].item())
+    wl.k_pool[:, page] = away[:, :, None, :].expand(s.L, s.Hkv, s.b, s.d).to(torch.bfloat16)
+    cfg = gb_config(s, max_slots=wl.max_slots)
+    ref = check_event(wl, cfg, check_f64=False)
+    assert ref["action"][0] == 0
+    for (r, l, h), d in ref["dropped"].items():
+        if r != 0:
+            continue
+        in_page = d[(d >= 512) & (d < 768)]
+        assert np.array_equal(in_page, np.arange(512, 704)), (l, h, in_page[:4], in_page.size)
+
+
+@needs_gpu
 @pytest.mark.parametrize("k_loc,reserve", [(0, 0), (64, 1), (120, 0)])
 def test_quota_and_reserve(k_loc, reserve):
     """k_loc = 0 (plain top-k), the default 64, and 120 (the largest quota that
