@@ -9,8 +9,8 @@
 // per destination row, kept with both addresses in a per-chunk table).
 // Slots before the first dropped one stay where they are.  Each source lies
 // at most b slots after its destination, so the workgroup walks destinations
-// in 256-row chunks: it loads a whole chunk into registers, waits for the
-// loads and barriers, then stores.  A chunk's stores land below every later
+// in 512-row chunks (128 KiB, 16 pieces of 16 bytes per thread): it loads a
+// whole chunk into registers, waits for the loads and barriers, then stores.  A chunk's stores land below every later
 // chunk's sources, and every earlier chunk has finished reading, so the
 // in-place move needs no copy of the row.  K and V rows, and different rows,
 // are disjoint and run as separate workgroups.
@@ -20,7 +20,9 @@ namespace gp {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCT = 256;                      // threads; one per dropped slot
+constexpr int kCT = 512;                      // threads
+constexpr int kPer = 16;                      // 16-byte pieces per thread per chunk
+constexpr int kRowsC = kCT * kPer / 16;       // destination rows per chunk (512)
 constexpr int kMaxPages = 65536 / kPage;      // pages per row held in LDS
 
 __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool_pages,
@@ -35,8 +37,8 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
                                                  int32_t* __restrict__ err) {
   __shared__ int32_t gap[kPage];
   __shared__ int32_t pg[kMaxPages];
-  __shared__ int64_t s_src[2][kCT];
-  __shared__ int64_t s_dst[2][kCT];
+  __shared__ int64_t s_src[2][kRowsC];
+  __shared__ int64_t s_dst[2][kRowsC];
   __shared__ int bad;
   if (!hdr->valid) return;
   const int LH = L * Hkv;
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
   const int t = threadIdx.x;
   if (t == 0) bad = 0;
   __syncthreads();
-  gap[t] = dropped[(int64_t)row * b + t] - t;
+  for (int k = t; k < kPage; k += kCT) gap[k] = dropped[(int64_t)row * b + k] - k;
   for (int i = t; i < P; i += kCT) {
     const int page = block_table[(int64_t)r * max_pages + i];
     if (page < 0 || page >= pool_pages) bad = 1;
@@ -69,13 +71,13 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
   const int end = (int)((P - 1) * b);
   const int d0 = gap[0] > 0 ? gap[0] : 0;
   int par = 0;
-  for (int c0 = d0; c0 < end; c0 += kCT, par ^= 1) {
-    // source and destination offsets of the chunk's 256 destination rows,
+  for (int c0 = d0; c0 < end; c0 += kRowsC, par ^= 1) {
+    // source and destination offsets of the chunk's destination rows,
     // one binary search per thread (tables alternate between two buffers so
     // the next chunk's tables never overwrite ones still being read)
     {
       const int drow = c0 + t;
-      if (drow < end) {
+      if (t < kRowsC && drow < end) {
         int lo = 0, hi = kPage;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
@@ -86,10 +88,10 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
       }
     }
     __syncthreads();
-    const int nrows = end - c0 < kCT ? end - c0 : kCT;
-    u32x4 v[16];
+    const int nrows = end - c0 < kRowsC ? end - c0 : kRowsC;
+    u32x4 v[kPer];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kPer; ++u) {
       const int piece = u * kCT + t;
       const int ri = piece >> 4, part = piece & 15;
       if (ri < nrows)
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kPer; ++u) {
       const int piece = u * kCT + t;
       const int ri = piece >> 4, part = piece & 15;
       if (ri < nrows) *reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8) = v[u];
