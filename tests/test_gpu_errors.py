@@ -1,0 +1,93 @@
+"""Error paths on the GPU, each forced from the host with inputs that the
+kernels' own checks catch (every kernel still runs to completion and no
+access leaves its buffers): the device error bits are set and the pool is left
+as it was where the event cannot proceed."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_04_amd import binding as gb
+from paged_kv_cache_04_amd import synth
+from gpu_util import device_rows, gb_config, log, run_stream_gpu, runner_for
+
+pytestmark = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU in this container")
+
+SMALL = synth.ModelShape("small", L=2, Hq=8, Hkv=2, theta=1e4)
+ERR_SLOT, ERR_POSITION, ERR_PAGE, ERR_SHORT, ERR_PAGES = 1, 2, 4, 8, 16
+
+
+def _workload(seed):
+    return synth.make_workload(SMALL, [4, 3], 16, seed=seed, device="cuda", align=["L", "S"],
+                               cluster_sizes=[20, 20], free_pages=0, steps=40, short_steps=8,
+                               max_slots=4)
+
+
+@needs_gpu
+def test_page_id_out_of_range():
+    """A block-table entry beyond the pool: scoring reads a valid page in its
+    place and flags PAGE; compaction of that request leaves its pages alone."""
+    log("test_page_id_out_of_range")
+    wl = _workload(41)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    good = wl.block_table[0, :4].cpu().numpy().copy()
+    k_before = device_rows(wl.k_pool, 1, 1, good)
+    wl.block_table[0, 2] = wl.k_pool.shape[1] + 5
+    run.demand(q)
+    run.grow()
+    run.compress()
+    torch.cuda.synchronize()
+    assert run.device_errors() & ERR_PAGE
+    assert int(run.action[0].item()) == 0  # pool full: fallback to compression
+    assert np.array_equal(device_rows(wl.k_pool, 1, 1, good), k_before)
+
+
+@needs_gpu
+def test_slot_and_position_out_of_range():
+    """A summary slot beyond the pool and a position beyond the rotary table:
+    the EMA update skips the request, calibration uses a zero scale and a
+    clamped position, and both bits are raised."""
+    log("test_slot_and_position_out_of_range")
+    wl = _workload(42)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    state_before = run.qstate.clone()
+    wl.slot[1] = wl.max_slots
+    wl.position[0] = wl.rope.shape[0] + 3
+    run.update(q, wl.first_step(wl.steps))
+    run.demand(q)
+    torch.cuda.synchronize()
+    bits = run.device_errors()
+    assert bits & ERR_SLOT and bits & ERR_POSITION, bits
+    # request 0's slot was updated, nothing else changed
+    s0 = int(wl.slot[0].item())
+    diff = (run.qstate != state_before).any(dim=(0, 2, 3, 4)).cpu().numpy()
+    assert diff[s0] and diff.sum() == 1
+
+
+@needs_gpu
+def test_stale_host_page_counts():
+    """The host mirror of the page counts disagrees with the device: the plan
+    rejects the batch, PAGES is raised, and no later kernel of the event runs
+    (outputs and pool untouched)."""
+    log("test_stale_host_page_counts")
+    wl = _workload(43)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    run.batch.num_pages_host[0] += 1
+    run.out.k_short.fill_(-7)
+    pages = wl.block_table[1, :3].cpu().numpy().copy()
+    k_before = device_rows(wl.k_pool, 0, 0, pages)
+    run.ws = torch.empty(gb.gp_workspace_bytes(run.ctx, 2, 8 * 256, 5 * 256), dtype=torch.uint8,
+                         device="cuda")
+    run.demand(q)
+    run.grow(decision=torch.zeros(2, dtype=torch.int8, device="cuda"))
+    run.compress()
+    torch.cuda.synchronize()
+    assert run.device_errors() & ERR_PAGES
+    assert (run.out.k_short == -7).all()
+    assert np.array_equal(device_rows(wl.k_pool, 0, 0, pages), k_before)

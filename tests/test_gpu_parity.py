@@ -88,6 +88,27 @@ def test_constant_keys_all_ties():
 
 
 @needs_gpu
+def test_max_batch_1024_requests():
+    """The largest batch the library takes (1024 requests), short ragged
+    requests of 2-4 pages, a few free pages so that some Grow decisions are
+    granted and the rest fall back: every output against the oracle."""
+    log("test_max_batch_1024_requests")
+    rng = np.random.default_rng(1024)
+    B = 1024
+    P = rng.integers(2, 5, size=B)
+    align = [str(a) for a in rng.choice(["S", "L"], size=B)]
+    wl = synth.make_workload(SMALL, P.tolist(), int(P.sum()) + 64, seed=1024, device="cuda",
+                             align=align, cluster_sizes=[12] * B, free_pages=40, steps=120,
+                             short_steps=16, max_slots=B)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    ref = check_event(wl, cfg, check_f64=False)
+    act = np.asarray(ref["action"])
+    n_grow = int((ref["dem"]["decision"] == 1).sum())
+    log(f"  {n_grow} Grow decisions")
+    assert (act == 1).sum() == min(n_grow, 40)
+
+
+@needs_gpu
 def test_junk_page_needs_block_quota():
     """One logical page of request 0 holds keys pointing away from both
     summary directions in every (layer, KV head): their attention underflows
