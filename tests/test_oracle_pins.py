@@ -417,6 +417,41 @@ def test_select_invariants(b, R, k_loc, P):
             assert np.array_equal(keep, want)
 
 
+def test_select_is_the_best_set_containing_the_block_quotas():
+    """Eq. 10 as an optimisation, by brute force on toy shapes (b = 8, R = 2,
+    P = 3): among all sets of K_t candidates that contain every block's
+    top-k_loc, the kept set is the one with the largest total importance.
+    Scores are distinct here, so that set is unique; it is found by
+    enumerating all C(|C \\ S_loc|, K_t - |S_loc|) completions."""
+    import itertools
+    rng = np.random.default_rng(2024)
+    b, R, P = 8, 2, 3
+    N = P * b
+    nc = N - R
+    kt = (P - 1) * b - R
+    for k_loc in (0, 1, 2, 3):
+        for trial in range(6):
+            s = rng.permutation(np.arange(1, N + 1)).astype(np.float32) / 64.0
+            aa = np.stack([s, s * 0.5], axis=1).astype(np.float32)
+            cfg = OracleConfig(L=1, Hq=1, Hkv=1, b=b, R=R, k_loc=k_loc)
+            keep = oracle.select(cfg, aa)
+            # block tops straight from the definition
+            sloc = set()
+            for j in range(P):
+                blk = [i for i in range(j * b, min((j + 1) * b, nc))]
+                sloc |= set(sorted(blk, key=lambda i: -s[i])[:min(k_loc, len(blk))])
+            rest = [i for i in range(nc) if i not in sloc]
+            best, best_sum = None, -1.0
+            for comb in itertools.combinations(rest, kt - len(sloc)):
+                tot = float(sum(s[i] for i in comb))
+                if tot > best_sum:
+                    best, best_sum = comb, tot
+            want = np.zeros(N, np.uint8)
+            want[list(sloc | set(best))] = 1
+            want[nc:] = 1
+            assert np.array_equal(keep, want), (k_loc, trial)
+
+
 def test_select_rejects_oversized_quota():
     cfg = OracleConfig(L=1, Hq=1, Hkv=1, b=8, R=2, k_loc=6)
     with pytest.raises(ValueError):
