@@ -10,7 +10,9 @@
 // Slots before the first dropped one stay where they are.  Each source lies
 // at most b slots after its destination, so the workgroup walks destinations
 // in 512-row chunks (128 KiB, 16 pieces of 16 bytes per thread): it loads a
-// whole chunk into registers, waits for the loads and barriers, then stores.  A chunk's stores land below every later
+// whole chunk into registers, waits for the loads and barriers, then stores.
+// Loads and stores are non-temporal: each byte is touched once, and keeping
+// it out of the caches leaves them to the next event's demand pass.  A chunk's stores land below every later
 // chunk's sources, and every earlier chunk has finished reading, so the
 // in-place move needs no copy of the row.  K and V rows, and different rows,
 // are disjoint and run as separate workgroups.
@@ -95,7 +97,8 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
       const int piece = u * kCT + t;
       const int ri = piece >> 4, part = piece & 15;
       if (ri < nrows)
-        v[u] = *reinterpret_cast<const u32x4*>(pool + s_src[par][ri] + part * 8);
+        v[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(pool + s_src[par][ri] + part * 8));
     }
     // every source of this chunk must be read before any of its stores
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -104,7 +107,9 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
     for (int u = 0; u < kPer; ++u) {
       const int piece = u * kCT + t;
       const int ri = piece >> 4, part = piece & 15;
-      if (ri < nrows) *reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8) = v[u];
+      if (ri < nrows)
+        __builtin_nontemporal_store(v[u],
+                                    reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8));
     }
   }
   if (lh == 0 && which == 0 && t == 0) num_tokens[r] = end;
