@@ -45,6 +45,7 @@ constexpr int kLdsBytes = kDW * kWaveStage;   // 147456, reused after scoring
 constexpr int kH1 = 2048;                     // first-digit buckets
 constexpr int kH2 = 1024;                     // second/third-digit buckets
 constexpr int kListCap = (kLdsBytes - 2 * kH1 * 8 - kH2 * 12) / 4;  // boundary members in LDS
+constexpr int kListHalf = kListCap / 2;                            // per view
 
 // acc[qi] += q[qi][e] * k[e] for e = 0..3 in order (4 bf16 keys in k).
 __device__ __forceinline__ void fma_quad(float* acc, const float* q, u32x2 k) {
@@ -224,15 +225,15 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
   __shared__ uint64_t s_red[kDW][2 * kNQ];
   __shared__ uint64_t s_W[2];
   __shared__ int s_item;
-  __shared__ int s_list_n;
-  __shared__ int s_dig;
-  __shared__ uint64_t s_mab;
-  __shared__ uint32_t s_cab;  // slots above the boundary so far
+  __shared__ int s_list_n[2];
+  __shared__ int s_dig[2];
+  __shared__ uint64_t s_mab[2];
+  __shared__ uint32_t s_cab[2];  // slots above the boundary so far, per view
   if (!a.hdr->valid) return;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int LH = a.L * a.Hkv;
-  const int64_t n_items = (int64_t)a.B * LH;
+  const int n_items = a.B * LH;  // <= 1024 requests x (L * Hkv) rows
   float* lg = a.ring_logits + (int64_t)blockIdx.x * a.ring_tokens * kNQ;
   float* rk = a.ring_keys + (int64_t)blockIdx.x * a.ring_tokens * 2;
   unsigned char* my = lds + w * kWaveStage;
@@ -252,7 +253,9 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     const int row = __builtin_amdgcn_readfirstlane(r * LH + lh);
     const int l = __builtin_amdgcn_readfirstlane(lh / a.Hkv);
     const int h = __builtin_amdgcn_readfirstlane(lh % a.Hkv);
-    const int64_t P = a.page_off[r + 1] - a.page_off[r];
+    // row sizes are block-uniform; read them into scalar registers so every
+    // branch and loop bound around the barriers below is a scalar branch
+    const int64_t P = __builtin_amdgcn_readfirstlane((int)(a.page_off[r + 1] - a.page_off[r]));
     const int64_t N = P * kPage, ndem = N - kPage;
     const int64_t row_tok = (int64_t)LH * a.page_off[r] * kPage + (int64_t)lh * N;
     const float* __restrict__ qv = qhat + (int64_t)row * (kNQ * kD);
@@ -500,46 +503,57 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     }
 
     // ---- 4. D_p of each view ------------------------------------------------------
+    // Runs for every row, including a single-page one (no candidates: its
+    // loops are empty and its outputs are forced to 0 at the end); no branch
+    // around this phase's barriers, so the row loop keeps one plain structure.
+    {
+    // first digit of both views (waves 0 and 1), then one pass over the key
+    // ring collects each view's boundary-bucket members into its half of the
+    // LDS list and counts the slots in buckets above it
+    if (w < 2) {
+      uint64_t mab = 0;
+      int d1;
+      scan_first_digit(h1m + w * kH1, s_W[w] * (uint64_t)a.p_num, (uint32_t)a.p_den, mab, d1);
+      if (lane == 0) {
+        s_dig[w] = d1;
+        s_mab[w] = mab;
+        s_cab[w] = 0;
+        s_list_n[w] = 0;
+      }
+    }
+    __syncthreads();
+    {
+      const uint32_t d0 = (uint32_t)s_dig[0], d1 = (uint32_t)s_dig[1];
+      uint32_t above0 = 0, above1 = 0;
+      for (int64_t i = t; i < ndem; i += kDT) {
+        const float2 kk = reinterpret_cast<const float2*>(rk)[i];
+        const uint32_t k0 = __float_as_uint(kk.x), k1 = __float_as_uint(kk.y);
+        above0 += (k0 >> 20) > d0;
+        above1 += (k1 >> 20) > d1;
+        if ((k0 >> 20) == d0) {
+          const int idx = atomicAdd(&s_list_n[0], 1);
+          if (idx < kListHalf) list[idx] = k0;
+        }
+        if ((k1 >> 20) == d1) {
+          const int idx = atomicAdd(&s_list_n[1], 1);
+          if (idx < kListHalf) list[kListHalf + idx] = k1;
+        }
+      }
+      above0 = wave_sum_u32(above0);
+      above1 = wave_sum_u32(above1);
+      if (lane == 0) {
+        atomicAdd(&s_cab[0], above0);
+        atomicAdd(&s_cab[1], above1);
+      }
+    }
+    __syncthreads();
     for (int x = 0; x < 2; ++x) {
       int32_t* outp = x == 0 ? a.k_short : a.k_long;
-      if (ndem <= 0) {
-        if (t == 0) outp[row] = 0;
-        continue;
-      }
       const uint64_t target = s_W[x] * (uint64_t)a.p_num;
-      if (w == 0) {
-        uint64_t mab = 0;
-        int d1;
-        scan_first_digit(h1m + x * kH1, target, (uint32_t)a.p_den, mab, d1);
-        if (lane == 0) {
-          s_dig = d1;
-          s_mab = mab;
-          s_cab = 0;
-          s_list_n = 0;
-        }
-      }
-      __syncthreads();
-      const uint32_t d1 = (uint32_t)s_dig;
-      uint32_t prefix = d1 << 20;
-      // members of the boundary bucket into LDS (as many as fit), and the
-      // number of slots in buckets above it
-      {
-        uint32_t above = 0;
-        for (int64_t i = t; i < ndem; i += kDT) {
-          const uint32_t key = __float_as_uint(rk[i * 2 + x]);
-          const uint32_t dig = key >> 20;
-          above += dig > d1;
-          if (dig == d1) {
-            const int idx = atomicAdd(&s_list_n, 1);
-            if (idx < kListCap) list[idx] = key;
-          }
-        }
-        above = wave_sum_u32(above);
-        if (lane == 0) atomicAdd(&s_cab, above);
-      }
-      __syncthreads();
-      const bool in_lds = s_list_n <= kListCap;
-      // digits 2 (bits 19..10) and 3 (bits 9..0)
+      const uint32_t* lst = list + x * kListHalf;
+      const bool in_lds = s_list_n[x] <= kListHalf;
+      uint32_t prefix = (uint32_t)s_dig[x] << 20;
+      // digits 2 (bits 19..10) and 3 (bits 9..0) over the bucket's members
       for (int pass = 0; pass < 2; ++pass) {
         const int shift = pass == 0 ? 10 : 0;
         const uint32_t mask = pass == 0 ? 0xfff00000u : 0xfffffc00u;
@@ -549,9 +563,9 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
         }
         __syncthreads();
         if (in_lds) {
-          const int n = s_list_n;
+          const int n = s_list_n[x];
           for (int k = t; k < n; k += kDT) {
-            const uint32_t key = list[k];
+            const uint32_t key = lst[k];
             if ((key & mask) == prefix) {
               const uint32_t dig = (key >> shift) & (kH2 - 1);
               atomicAdd(&h2c[dig], 1u);
@@ -572,26 +586,29 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
         }
         __syncthreads();
         if (w == 0) {
-          uint64_t mab = s_mab;
-          uint32_t cab = s_cab;
+          uint64_t mab = s_mab[x];
+          uint32_t cab = s_cab[x];
           int dd;
           scan_desc<kH2>(h2c, h2m, target, (uint32_t)a.p_den, mab, cab, dd);
           if (lane == 0) {
-            s_dig = dd;
-            s_mab = mab;
-            s_cab = cab;
+            s_dig[x] = dd;
+            s_mab[x] = mab;
+            s_cab[x] = cab;
           }
         }
         __syncthreads();
-        prefix |= (uint32_t)s_dig << shift;
+        prefix |= (uint32_t)s_dig[x] << shift;
       }
       if (t == 0) {
-        const uint64_t wt = fix40(__uint_as_float(prefix));
-        const uint64_t need = target - s_mab * (uint64_t)a.p_den;
+        const bool has = ndem > 0;
+        const uint64_t wt = fix40(__uint_as_float(has ? prefix : 0u));
+        const uint64_t need = target - s_mab[x] * (uint64_t)a.p_den;
         const uint64_t den = wt * (uint64_t)a.p_den;
-        outp[row] = (int32_t)(s_cab + (need + den - 1) / den);
+        const uint64_t rest = den != 0 ? (need + den - 1) / den : 0;
+        outp[row] = has ? (int32_t)(s_cab[x] + rest) : 0;
       }
       __syncthreads();
+    }
     }
   }
 }
