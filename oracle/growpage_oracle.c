@@ -31,6 +31,7 @@
 
 #define ORC_GROW 1
 #define ORC_COMPRESS 0
+#define ORC_SHRINK 2
 
 static float bf16_value(uint16_t h) {
   uint32_t u = (uint32_t)h << 16;
@@ -308,13 +309,40 @@ int orc_decide(const int32_t* ks, const int32_t* kl, int n_rows,
 }
 
 /* ------------------------------------------------------------------------
+ * The three-way GrowPage-Shrink rule (Appendix H.1 Eq. 13), on the same
+ * Delta as orc_decide:
+ *   Delta > tau                    -> Grow by One Page
+ *   shrink_tau <= Delta <= tau     -> Compress & Hold
+ *   Delta < shrink_tau             -> Shrink, unless the capacity left after
+ *                                     it, (P - 1) b, would fall below
+ *                                     min_tokens (then Compress & Hold).
+ * Shrink drops two pages worth of slots and returns one page to the pool
+ * (orc_select_pages with 2 pages, orc_return_pages).  A request of one page
+ * grows, as in orc_decide.
+ * Pins: the three regions, both boundaries (Delta = shrink_tau and
+ * Delta = tau are Compress & Hold), the capacity floor.
+ * ---------------------------------------------------------------------- */
+int orc_decide_shrink(const int32_t* ks, const int32_t* kl, int n_rows,
+                      int64_t card_c, int num_pages, int b, double tau,
+                      double shrink_tau, int min_tokens, int64_t* diff_out,
+                      double* delta_out) {
+  double delta = 0.0;
+  const int base = orc_decide(ks, kl, n_rows, card_c, tau, diff_out, &delta);
+  if (delta_out) *delta_out = delta;
+  if (base == ORC_GROW) return ORC_GROW;
+  if (delta < shrink_tau && (int64_t)(num_pages - 1) * b >= min_tokens) return ORC_SHRINK;
+  return ORC_COMPRESS;
+}
+
+/* ------------------------------------------------------------------------
  * Grow by One Page with fallback (§3.3 "Grow by One Page"; §4.2 "Scheduler-
  * Aware Page Allocation and Fallback"; Appendix H.2 defines a fallback).
  * Requests are served in index order.  A growing request takes the page on
  * top of the free stack (free_stack[free_count - 1]) while more than
  * `reserve` pages are free and its block table has room, appends it to its
  * block table and increments its page count.  Otherwise it falls back to
- * Compress & Hold.  action[r] = 1 grown, 0 compress (incl. fallback).
+ * Compress & Hold.  action[r] = 1 grown, 0 compress (incl. fallback); a
+ * Shrink decision (orc_decide_shrink) passes through as action 2.
  * counters: [0] pages granted, [1] compress actions, [2] fallbacks.
  * ---------------------------------------------------------------------- */
 void orc_grow(const int8_t* decision, int B, int32_t* block_table,
@@ -335,6 +363,8 @@ void orc_grow(const int8_t* decision, int B, int32_t* block_table,
         counters[1] += 1;
         counters[2] += 1;
       }
+    } else if (decision[r] == ORC_SHRINK) {
+      action[r] = ORC_SHRINK;  /* needs no page; orc_return_pages frees one */
     } else {
       action[r] = 0;
       counters[1] += 1;
@@ -349,9 +379,10 @@ void orc_grow(const int8_t* decision, int B, int32_t* block_table,
  * mask, §3.3 and §5.1: 16 tokens).  Blocks B_j = C intersected with logical
  * page j.  Order: larger s first; equal s, larger slot (newer token) first.
  *   S_loc = union over j of the top-min(k_loc, |B_j|) of B_j;
- *   K_t   = (P - 1) b - R  (one page of slots is freed);
+ *   K_t   = (P - m) b - R  (m pages of slots are freed: 1 for Compress &
+ *           Hold, 2 for Shrink; orc_select is m = 1);
  *   S     = S_loc plus the top-(K_t - |S_loc|) of C \ S_loc;
- *   kept  = S plus the window.  |kept| = (P - 1) b.
+ *   kept  = S plus the window.  |kept| = (P - m) b.
  * abar_all is [N][2]; keep is [N] (1 kept, 0 dropped).
  * Returns 0, or -1 when |S_loc| > K_t (the quota cannot fit the budget).
  * Pins: count, window, per-block quota, dominance of picks over drops,
@@ -370,11 +401,11 @@ static int cmp_cand_desc(const void* a, const void* b) {
   return x->slot > y->slot ? -1 : (x->slot < y->slot);
 }
 
-int orc_select(const float* abar_all, int N, int b, int R, int k_loc,
-               uint8_t* keep) {
+int orc_select_pages(const float* abar_all, int N, int b, int R, int k_loc,
+                     int freed_pages, uint8_t* keep) {
   const int P = N / b;
   const int nc = N - R;
-  const int kt = (P - 1) * b - R;
+  const int kt = (P - freed_pages) * b - R;
   float* s = (float*)malloc(sizeof(float) * (size_t)N);
   for (int i = 0; i < N; ++i) s[i] = fmaxf(abar_all[(size_t)i * 2], abar_all[(size_t)i * 2 + 1]);
   orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(nc > 0 ? nc : 1));
@@ -410,6 +441,37 @@ int orc_select(const float* abar_all, int N, int b, int R, int k_loc,
   free(c);
   free(s);
   return 0;
+}
+
+int orc_select(const float* abar_all, int N, int b, int R, int k_loc,
+               uint8_t* keep) {
+  return orc_select_pages(abar_all, N, b, R, k_loc, 1, keep);
+}
+
+/* ------------------------------------------------------------------------
+ * Page return of Shrink (Appendix H.1): after the two-page compaction a
+ * shrinking request keeps its first P - 1 pages; the last one goes back to
+ * the global pool.  Requests are served in index order, each pushing its
+ * page on top of the free stack (so a later Grow takes the most recently
+ * returned page first); the block-table entry is cleared to -1 and P
+ * decreases by one.  Requests with fewer than 3 pages are left alone.
+ * Returns the number of pages returned.
+ * Pins: pool arithmetic and order.
+ * ---------------------------------------------------------------------- */
+int orc_return_pages(const int8_t* action, int B, int32_t* block_table,
+                     int max_pages, int32_t* num_pages, int32_t* free_stack,
+                     int32_t* free_count) {
+  int n = 0;
+  for (int r = 0; r < B; ++r) {
+    if (action[r] != ORC_SHRINK || num_pages[r] < 3) continue;
+    const size_t at = (size_t)r * max_pages + (num_pages[r] - 1);
+    free_stack[*free_count] = block_table[at];
+    *free_count += 1;
+    block_table[at] = -1;
+    num_pages[r] -= 1;
+    ++n;
+  }
+  return n;
 }
 
 /* ------------------------------------------------------------------------

@@ -26,6 +26,7 @@ from . import build as _build
 
 GROW = 1
 COMPRESS = 0
+SHRINK = 2
 
 _LIB = None
 
@@ -61,6 +62,13 @@ def lib():
         L.orc_grow.restype = None
         L.orc_select.argtypes = [f32p, c_int, c_int, c_int, c_int, u8p]
         L.orc_select.restype = c_int
+        L.orc_select_pages.argtypes = [f32p, c_int, c_int, c_int, c_int, c_int, u8p]
+        L.orc_select_pages.restype = c_int
+        L.orc_decide_shrink.argtypes = [i32p, i32p, c_int, ctypes.c_int64, c_int, c_int, c_double,
+                                        c_double, c_int, i64p, ctypes.POINTER(c_double)]
+        L.orc_decide_shrink.restype = c_int
+        L.orc_return_pages.argtypes = [i8p, c_int, i32p, c_int, i32p, i32p, i32p]
+        L.orc_return_pages.restype = c_int
         L.orc_compact.argtypes = [u16p, u8p, c_int, c_int]
         L.orc_compact.restype = c_int
         _LIB = L
@@ -88,6 +96,9 @@ class OracleConfig:
     alpha_s: float = 0.1    # 1 - beta_S, beta_S = 0.9 (§3.2 Eq. 6)
     alpha_l: float = 0.001  # 1 - beta_L, beta_L = 0.999
     M: int = 512            # query slots (Appendix E.1)
+    policy: int = 0         # 0: Grow or Compress & Hold (section 3); 1: GrowPage-Shrink (App. H.1)
+    shrink_tau: float = -0.005  # Eq. 13 shrink threshold (App. H.1)
+    min_tokens: int = 1024  # capacity floor of Shrink (App. H.1)
 
     @property
     def G(self) -> int:
@@ -161,14 +172,24 @@ def row(cfg: OracleConfig, keys: np.ndarray, qh: np.ndarray, want_logits: bool =
     return RowResult(dp=dpo, abar_all=aa, abar_dem=ad[:ndem], logits=lg)
 
 
-def decide(cfg: OracleConfig, ks: np.ndarray, kl: np.ndarray, card_c: int):
-    """A5 for one request: returns (decision, diff, delta)."""
+def decide(cfg: OracleConfig, ks: np.ndarray, kl: np.ndarray, card_c: int,
+           num_pages: int | None = None):
+    """A5 for one request: returns (decision, diff, delta).  With
+    cfg.policy == 1 the three-way Shrink rule (needs num_pages)."""
     ks = np.ascontiguousarray(ks, dtype=np.int32).ravel()
     kl = np.ascontiguousarray(kl, dtype=np.int32).ravel()
     diff = ctypes.c_int64()
     delta = ctypes.c_double()
-    dec = lib().orc_decide(_p(ks, ctypes.c_int32), _p(kl, ctypes.c_int32), ks.size, int(card_c),
-                           float(cfg.tau), ctypes.byref(diff), ctypes.byref(delta))
+    if cfg.policy == 1:
+        P = int(card_c) // cfg.b + 1 if num_pages is None else int(num_pages)
+        dec = lib().orc_decide_shrink(_p(ks, ctypes.c_int32), _p(kl, ctypes.c_int32), ks.size,
+                                      int(card_c), P, cfg.b, float(cfg.tau),
+                                      float(cfg.shrink_tau), int(cfg.min_tokens),
+                                      ctypes.byref(diff), ctypes.byref(delta))
+    else:
+        dec = lib().orc_decide(_p(ks, ctypes.c_int32), _p(kl, ctypes.c_int32), ks.size,
+                               int(card_c), float(cfg.tau), ctypes.byref(diff),
+                               ctypes.byref(delta))
     return int(dec), int(diff.value), float(delta.value)
 
 
@@ -189,17 +210,34 @@ def grow(decision: np.ndarray, block_table: np.ndarray, num_pages: np.ndarray,
 
 
 def select(cfg: OracleConfig, abar_all: np.ndarray, k_loc: int | None = None,
-           b: int | None = None, R: int | None = None) -> np.ndarray:
-    """A7-A8 for one row: returns keep [N] uint8."""
+           b: int | None = None, R: int | None = None, pages: int = 1) -> np.ndarray:
+    """A7-A8 for one row: returns keep [N] uint8.  pages = slots freed in
+    pages: 1 for Compress & Hold, 2 for Shrink."""
     abar_all = np.ascontiguousarray(abar_all, dtype=np.float32)
     N = abar_all.shape[0]
     keep = np.empty(N, dtype=np.uint8)
-    rc = lib().orc_select(_p(abar_all, ctypes.c_float), N, cfg.b if b is None else b,
-                          cfg.R if R is None else R, cfg.k_loc if k_loc is None else k_loc,
-                          _p(keep, ctypes.c_uint8))
+    rc = lib().orc_select_pages(_p(abar_all, ctypes.c_float), N, cfg.b if b is None else b,
+                                cfg.R if R is None else R,
+                                cfg.k_loc if k_loc is None else k_loc, int(pages),
+                                _p(keep, ctypes.c_uint8))
     if rc != 0:
         raise ValueError("local quota exceeds the retention budget")
     return keep
+
+
+def return_pages(action: np.ndarray, block_table: np.ndarray, num_pages: np.ndarray,
+                 free_stack: np.ndarray, free_count: int):
+    """Shrink's page return, in place on block_table / num_pages /
+    free_stack.  Returns (pages returned, free_count)."""
+    action = np.ascontiguousarray(action, dtype=np.int8)
+    B, max_pages = block_table.shape
+    assert block_table.dtype == np.int32 and num_pages.dtype == np.int32
+    assert free_stack.dtype == np.int32 and free_stack.flags["C_CONTIGUOUS"]
+    fc = np.array([free_count], dtype=np.int32)
+    n = lib().orc_return_pages(_p(action, ctypes.c_int8), B, _p(block_table, ctypes.c_int32),
+                               max_pages, _p(num_pages, ctypes.c_int32),
+                               _p(free_stack, ctypes.c_int32), _p(fc, ctypes.c_int32))
+    return int(n), int(fc[0])
 
 
 def compact(rows: np.ndarray, keep: np.ndarray) -> int:
@@ -245,7 +283,7 @@ def demand(cfg: OracleConfig, get_keys, block_table, num_pages, state, qcur, rop
                 ks[r, l, h], kl[r, l, h] = res.dp
                 if want_abar:
                     abar[(r, l, h)] = res.abar_all
-        decision[r], diff[r], delta[r] = decide(cfg, ks[r], kl[r], (P - 1) * cfg.b)
+        decision[r], diff[r], delta[r] = decide(cfg, ks[r], kl[r], (P - 1) * cfg.b, P)
     return dict(ks=ks, kl=kl, decision=decision, diff=diff, delta=delta, abar=abar)
 
 

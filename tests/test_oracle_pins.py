@@ -346,6 +346,47 @@ def test_decide_sign_and_eq8_mean():
     assert oracle.decide(cfg, np.array([1]), np.array([9]), 0)[0] == oracle.GROW
 
 
+def test_decide_shrink_three_regions():
+    """orc_decide_shrink (Appendix H.1 Eq. 13): Shrink below -0.005, Compress
+    & Hold on [-0.005, 0] (both ends included), Grow above 0; Shrink only
+    when (P - 1) b >= 1024 tokens remain; a one-page request grows."""
+    cfg = OracleConfig(L=1, Hq=4, Hkv=1, b=200, policy=1, min_tokens=1000)
+    one = np.array([0], np.int32)
+    # P = 6, b = 200: |C_t| = 1000, Delta = diff / 1000 with one row
+    for diff, want in ((-7, oracle.SHRINK), (-6, oracle.SHRINK), (-5, oracle.COMPRESS),
+                       (-4, oracle.COMPRESS), (0, oracle.COMPRESS), (1, oracle.GROW)):
+        dec, d, delta = oracle.decide(cfg, np.array([diff], np.int32) if diff >= 0 else one,
+                                      one if diff >= 0 else np.array([-diff], np.int32), 1000, 6)
+        assert d == diff and delta == diff / 1000.0
+        assert dec == want, (diff, dec)
+    # capacity floor: with b = 256, P = 5 leaves 1024 tokens, P = 4 only 768
+    cfg = OracleConfig(L=1, Hq=4, Hkv=1, b=256, policy=1)
+    assert oracle.decide(cfg, one, np.array([900], np.int32), 4 * 256, 5)[0] == oracle.SHRINK
+    assert oracle.decide(cfg, one, np.array([900], np.int32), 3 * 256, 4)[0] == oracle.COMPRESS
+    assert oracle.decide(cfg, one, np.array([9], np.int32), 0, 1)[0] == oracle.GROW
+    # the default policy never shrinks
+    cfg = OracleConfig(L=1, Hq=4, Hkv=1, b=256)
+    assert oracle.decide(cfg, one, np.array([900], np.int32), 4 * 256, 5)[0] == oracle.COMPRESS
+
+
+def test_return_pages_pool_arithmetic():
+    """orc_return_pages (Appendix H.1): shrinking requests, in index order,
+    push their last page on top of the free stack, clear that block-table
+    entry and lose one page; requests below 3 pages and other actions are
+    untouched; free_after = free_before + returned."""
+    B, maxp = 5, 6
+    bt = (np.arange(B * maxp, dtype=np.int32).reshape(B, maxp) + 100)
+    P = np.array([5, 4, 2, 6, 3], np.int32)
+    action = np.array([2, 0, 2, 2, 1], np.int8)
+    stack = np.full(12, -7, np.int32)
+    stack[:3] = [1, 2, 3]
+    n, fc = oracle.return_pages(action, bt, P, stack, 3)
+    assert n == 2 and fc == 5
+    assert list(stack[:5]) == [1, 2, 3, 104, 123]
+    assert bt[0, 4] == -1 and bt[3, 5] == -1 and bt[2, 1] == 113
+    assert list(P) == [4, 4, 2, 5, 3]
+
+
 # ------------------------------------------------------------------ grow --
 
 def test_grow_pool_arithmetic_and_fallback():
@@ -372,11 +413,11 @@ def test_grow_pool_arithmetic_and_fallback():
 
 # ---------------------------------------------------------------- select --
 
-def _check_selection(s, keep, N, b, R, k_loc):
+def _check_selection(s, keep, N, b, R, k_loc, pages=1):
     """Invariants that fix Eq. 10's kept set uniquely for a total order."""
     P = N // b
     nc = N - R
-    assert keep.sum() == (P - 1) * b
+    assert keep.sum() == (P - pages) * b
     assert np.all(keep[nc:] == 1)
     key = lambda i: (s[i], i)
     sloc = set()
@@ -446,6 +487,48 @@ def test_select_is_the_best_set_containing_the_block_quotas():
                 tot = float(sum(s[i] for i in comb))
                 if tot > best_sum:
                     best, best_sum = comb, tot
+            want = np.zeros(N, np.uint8)
+            want[list(sloc | set(best))] = 1
+            want[nc:] = 1
+            assert np.array_equal(keep, want), (k_loc, trial)
+
+
+@pytest.mark.parametrize("b,R,k_loc,P", [(8, 2, 2, 4), (8, 2, 0, 3), (16, 4, 3, 5), (256, 16, 64, 5)])
+def test_select_two_pages_invariants(b, R, k_loc, P):
+    """orc_select_pages with 2 pages (Shrink, Appendix H.1): the same Eq. 10
+    invariants with the budget K_t = (P - 2) b - R, so 2b candidates are
+    dropped."""
+    rng = np.random.default_rng(b * 31 + P)
+    N = P * b
+    cfg = OracleConfig(L=1, Hq=1, Hkv=1, b=b, R=R, k_loc=k_loc)
+    for trial in range(10):
+        q = int(rng.choice([4, 1 << 20]))
+        aa = (np.floor(rng.random((N, 2)) * q) / q).astype(np.float32)
+        keep = oracle.select(cfg, aa, pages=2)
+        _check_selection(np.maximum(aa[:, 0], aa[:, 1]), keep, N, b, R, k_loc, pages=2)
+        assert (keep[:N - R] == 0).sum() == 2 * b
+
+
+def test_select_two_pages_is_the_best_completion():
+    """The 2-page selection as an optimisation, by brute force (b = 8, R = 2,
+    P = 3): the best-total completion of the block quotas to K_t = 6."""
+    import itertools
+    rng = np.random.default_rng(77)
+    b, R, P = 8, 2, 3
+    N, nc, kt = P * b, P * b - R, (P - 2) * b - R
+    for k_loc in (0, 1):
+        for trial in range(4):
+            s = rng.permutation(np.arange(1, N + 1)).astype(np.float32) / 64.0
+            aa = np.stack([s * 0.25, s], axis=1).astype(np.float32)
+            keep = oracle.select(OracleConfig(L=1, Hq=1, Hkv=1, b=b, R=R, k_loc=k_loc), aa,
+                                 pages=2)
+            sloc = set()
+            for j in range(P):
+                blk = list(range(j * b, min((j + 1) * b, nc)))
+                sloc |= set(sorted(blk, key=lambda i: -s[i])[:min(k_loc, len(blk))])
+            rest = [i for i in range(nc) if i not in sloc]
+            best = max(itertools.combinations(rest, kt - len(sloc)),
+                       key=lambda c: float(sum(s[i] for i in c)))
             want = np.zeros(N, np.uint8)
             want[list(sloc | set(best))] = 1
             want[nc:] = 1
