@@ -70,6 +70,11 @@ enum gp_err_bits {
 /* Actions and decisions (int8 on the device). */
 #define GP_COMPRESS 0
 #define GP_GROW 1
+#define GP_SHRINK 2 /* GrowPage-Shrink policy only (App. H.1 Eq. 13) */
+
+/* Capacity policies (gp_config.policy). */
+#define GP_POLICY_GROWPAGE 0 /* Grow by One Page or Compress & Hold (§3.2-3.3) */
+#define GP_POLICY_SHRINK 1   /* adds Shrink below shrink_tau (App. H.1 Eq. 13) */
 
 /* Method parameters; defaults in brackets are the pages'. */
 typedef struct gp_config {
@@ -85,6 +90,11 @@ typedef struct gp_config {
   float alpha_short;     /* new-query weight 1 - beta_S [0.1] (§3.2 Eq. 6) */
   float alpha_long;      /* new-query weight 1 - beta_L [0.001] */
   int32_t max_slots;     /* M, query-state slots [512] (App. E.1) */
+  int32_t policy;        /* GP_POLICY_GROWPAGE [default] or GP_POLICY_SHRINK */
+  double shrink_tau;     /* Shrink iff Delta < shrink_tau [-0.005] (App. H.1 Eq. 13);
+                            must be <= tau; used by GP_POLICY_SHRINK only */
+  int32_t min_tokens;    /* capacity floor: Shrink only if (P - 1) b >= min_tokens
+                            [1024] (App. H.1) */
 } gp_config;
 
 /* Global page pool (§4.2): K/V storage and the device free-page stack. */
@@ -101,8 +111,10 @@ typedef struct gp_batch {
   int32_t batch;                 /* B */
   int32_t max_pages;             /* row stride of block_table */
   int32_t* block_table;          /* device int32 [B][max_pages] page ids */
-  int32_t* num_pages;            /* device int32 [B] P (gp_grow_page increments) */
-  int32_t* num_tokens;           /* device int32 [B] N (gp_compress_hold writes (P-1) b) */
+  int32_t* num_pages;            /* device int32 [B] P (gp_grow_page increments,
+                                    gp_compress_hold decrements on Shrink) */
+  int32_t* num_tokens;           /* device int32 [B] N (gp_compress_hold writes (P-1) b,
+                                    or (P-2) b on Shrink) */
   const int32_t* slot;           /* device int32 [B] query-state slot */
   const int32_t* position;       /* device int32 [B] absolute position of the current query */
   const int32_t* num_pages_host; /* host int32 [B], equal to num_pages at the call */
@@ -114,7 +126,9 @@ typedef struct gp_demand_out {
   int32_t* k_long;   /* [B][L][Hkv] K^L */
   int64_t* k_diff;   /* [B] sum K^S - sum K^L (may be NULL) */
   double* delta;     /* [B] Delta_t = r^S - r^L (Eq. 8) (may be NULL) */
-  int8_t* decision;  /* [B] GP_GROW iff Delta_t > tau, else GP_COMPRESS */
+  int8_t* decision;  /* [B] GP_GROW iff Delta_t > tau, else GP_COMPRESS; with
+                        GP_POLICY_SHRINK, GP_SHRINK iff Delta_t < shrink_tau and
+                        (P - 1) b >= min_tokens */
   float* abar;       /* optional [sum over rows of N][2]: the full-cache attention
                         distributions (short, long) per token, rows in (request,
                         layer, KV head) order; NULL skips the write */
@@ -124,13 +138,15 @@ typedef struct gp_counters {
   int64_t grown;     /* pages granted by gp_grow_page */
   int64_t compress;  /* Compress & Hold actions (decisions plus fallbacks) */
   int64_t fallback;  /* Grow decisions that fell back (§4.2, App. H.2) */
+  int64_t shrunk;    /* pages returned to the pool by Shrink (App. H.1) */
 } gp_counters;
 
 typedef struct gp_ctx gp_ctx;
 
 /* Creates a context on the current HIP device.  Validates the config:
  * Hq % Hkv == 0, 0 <= recent_window < page_size, local_quota >= 0,
- * 0 < p_num <= p_den <= 2^20, 0 < alpha <= 1, max_slots >= 1. */
+ * 0 < p_num <= p_den <= 2^20, 0 < alpha <= 1, max_slots >= 1, policy one of
+ * GP_POLICY_*, shrink_tau <= tau, min_tokens >= 0. */
 gp_status gp_create(const gp_config* cfg, gp_ctx** out);
 void gp_destroy(gp_ctx* ctx);
 
@@ -171,8 +187,9 @@ gp_status gp_demand(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
  * top of the free stack while more than reserve_pages are free and its block
  * table has room; the page is appended to its block table and P += 1.
  * Otherwise it falls back to compression.  action[b] receives GP_GROW or
- * GP_COMPRESS; decision may come from gp_demand or from the caller (policy
- * variants).  Page counts never decrease (§3.3). */
+ * GP_COMPRESS, or GP_SHRINK for a GP_SHRINK decision (no page is taken);
+ * decision may come from gp_demand or from the caller (policy variants).
+ * Under GP_POLICY_GROWPAGE page counts never decrease (§3.3). */
 gp_status gp_grow_page(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
                        const int8_t* decision, int8_t* action,
                        int32_t reserve_pages, void* stream);
@@ -185,10 +202,17 @@ gp_status gp_grow_page(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
  * to the globally most important remaining candidates (ties: newer slot
  * first); exactly b candidates are dropped and the kept K/V rows move, in
  * slot order, to slots 0 .. (P-1) b - 1 of the same pages.  num_tokens
- * becomes (P-1) b; block tables and P are unchanged.  Must follow gp_demand
- * on the same batch with the same workspace.  dropped_out (optional, device
- * int32 [B][L][Hkv][b]) receives the dropped slots in ascending order; rows of
- * requests that do not compress are left unwritten. */
+ * becomes (P-1) b; block tables and P are unchanged.  A request whose action
+ * is GP_SHRINK (App. H.1) drops 2b candidates instead (budget (P-2) b -
+ * recent_window), its kept rows move to slots 0 .. (P-2) b - 1, then its last
+ * page is pushed on the free stack (requests in index order), its block-table
+ * entry set to -1, P -= 1 and num_tokens = (P-2) b with the old P; a Shrink
+ * with fewer than 3 pages sets GP_DEVERR_SHORT and leaves the request as it
+ * was; under GP_POLICY_GROWPAGE a GP_SHRINK action is ignored.  Must follow gp_demand on the same batch with the same workspace.
+ * dropped_out (optional, device int32 [B][L][Hkv][b] under
+ * GP_POLICY_GROWPAGE, [B][L][Hkv][2b] under GP_POLICY_SHRINK) receives the
+ * dropped slots in ascending order; rows of requests that do not compress
+ * are left unwritten. */
 gp_status gp_compress_hold(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
                            const int8_t* action, void* workspace,
                            size_t workspace_bytes, int32_t* dropped_out,
@@ -204,7 +228,8 @@ enum gp_kernel_id {
   GP_K_GROW = 5,    /* A6 page grant and fallback */
   GP_K_SELECT = 6,  /* A7-A8 window mask and Eq. 10 selection */
   GP_K_COMPACT = 7, /* A9 in-place compaction */
-  GP_NUM_KERNELS = 8
+  GP_K_RETURN = 8,  /* Shrink's page return (GP_POLICY_SHRINK only) */
+  GP_NUM_KERNELS = 9
 };
 
 typedef struct gp_kernel_times {

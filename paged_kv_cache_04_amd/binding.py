@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrowpage
 
 GP_COMPRESS = 0
 GP_GROW = 1
+GP_SHRINK = 2
+GP_POLICY_GROWPAGE = 0
+GP_POLICY_SHRINK = 1
 
 SYMBOLS = (
     "gp_create", "gp_destroy", "gp_workspace_bytes", "gp_update_summaries", "gp_demand",
@@ -25,7 +28,7 @@ SYMBOLS = (
     "gp_status_str", "gp_last_hip_error", "gp_profile", "gp_profile_read",
 )
 
-KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact")
+KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact", "return")
 
 
 class GPError(RuntimeError):
@@ -40,6 +43,8 @@ class gp_config(ctypes.Structure):
         ("local_quota", ctypes.c_int32), ("p_num", ctypes.c_int32), ("p_den", ctypes.c_int32),
         ("tau", ctypes.c_double), ("alpha_short", ctypes.c_float),
         ("alpha_long", ctypes.c_float), ("max_slots", ctypes.c_int32),
+        ("policy", ctypes.c_int32), ("shrink_tau", ctypes.c_double),
+        ("min_tokens", ctypes.c_int32),
     ]
 
 
@@ -67,12 +72,12 @@ class gp_demand_out(ctypes.Structure):
 
 
 class gp_kernel_times(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 8), ("launches", ctypes.c_int64 * 8)]
+    _fields_ = [("ms", ctypes.c_double * len(KERNELS)), ("launches", ctypes.c_int64 * len(KERNELS))]
 
 
 class gp_counters(ctypes.Structure):
     _fields_ = [("grown", ctypes.c_int64), ("compress", ctypes.c_int64),
-                ("fallback", ctypes.c_int64)]
+                ("fallback", ctypes.c_int64), ("shrunk", ctypes.c_int64)]
 
 
 _lib = None
@@ -161,6 +166,14 @@ class Config:
     alpha_short: float = 0.1
     alpha_long: float = 0.001
     max_slots: int = 512
+    policy: int = GP_POLICY_GROWPAGE
+    shrink_tau: float = -0.005
+    min_tokens: int = 1024
+
+    @property
+    def max_freed(self) -> int:
+        """Pages of slots one event can free per request (2 with Shrink)."""
+        return 2 if self.policy == GP_POLICY_SHRINK else 1
 
 
 class Context:
@@ -172,7 +185,7 @@ class Context:
         c = gp_config(cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                       cfg.page_size, cfg.recent_window, cfg.local_quota, cfg.p_num, cfg.p_den,
                       float(cfg.tau), float(cfg.alpha_short), float(cfg.alpha_long),
-                      cfg.max_slots)
+                      cfg.max_slots, cfg.policy, float(cfg.shrink_tau), cfg.min_tokens)
         h = ctypes.c_void_p()
         _check(L.gp_create(ctypes.byref(c), ctypes.byref(h)), "gp_create")
         self.handle = h
@@ -280,7 +293,7 @@ def gp_compress_hold(ctx: Context, pool: Pool, batch: Batch, action, workspace,
 def gp_get_counters(ctx: Context) -> dict:
     c = gp_counters()
     _check(load().gp_get_counters(ctx.handle, ctypes.byref(c)), "gp_get_counters", ctx)
-    return dict(grown=c.grown, compress=c.compress, fallback=c.fallback)
+    return dict(grown=c.grown, compress=c.compress, fallback=c.fallback, shrunk=c.shrunk)
 
 
 def gp_get_device_errors(ctx: Context) -> int:

@@ -12,7 +12,7 @@ struct gp_ctx {
   gp::Params p;
   int device = 0;
   int num_cus = 256;
-  int64_t* d_counters = nullptr;  // [3]
+  int64_t* d_counters = nullptr;  // [4]: granted, compress, fallback, returned
   int32_t* d_err = nullptr;       // [1], right after the counters
   int last_hip = 0;
   // bookkeeping of the last gp_demand, checked by gp_compress_hold
@@ -108,6 +108,13 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
   p.alpha_s = cfg->alpha_short;
   p.alpha_l = cfg->alpha_long;
   p.M = cfg->max_slots;
+  p.policy = cfg->policy;
+  p.shrink_tau = cfg->shrink_tau;
+  p.min_tokens = cfg->min_tokens;
+  if (p.policy != GP_POLICY_GROWPAGE && p.policy != GP_POLICY_SHRINK) return GP_ERR_INVALID_ARG;
+  if (p.policy == GP_POLICY_SHRINK &&
+      (!(p.shrink_tau <= p.tau) || p.min_tokens < 0))
+    return GP_ERR_INVALID_ARG;
   if (p.L < 1 || p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0 || p.d < 2 || p.d % 2 != 0 ||
       p.b < 1 || p.R < 0 || p.R >= p.b || p.kloc < 0 || p.p_num <= 0 || p.p_den < p.p_num ||
       p.p_den > (1 << 20) || !(p.alpha_s > 0.0f && p.alpha_s <= 1.0f) ||
@@ -126,7 +133,7 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
     delete c;
     return GP_ERR_HIP;
   }
-  c->d_err = reinterpret_cast<int32_t*>(c->d_counters + 3);
+  c->d_err = reinterpret_cast<int32_t*>(c->d_counters + 4);
   *out = c;
   return GP_OK;
 }
@@ -235,14 +242,20 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   if (!ws || ws != c->ws || ws_bytes != c->ws_bytes || bt->batch != c->batch)
     return GP_ERR_WORKSPACE;
   const gp::Params& p = c->p;
-  // Eq. 10 needs the local quotas to fit the budget K_t = (P - 1) b - R.
+  if (p.policy == GP_POLICY_SHRINK && action &&
+      (!pool->free_stack || !pool->free_count || !bt->num_pages || pool->num_pages < 1))
+    return GP_ERR_INVALID_ARG;
+  // Eq. 10 needs the local quotas to fit the budget K_t = (P - m) b - R,
+  // m = 1 for Compress & Hold, 2 for Shrink (any request with 3 or more pages
+  // may shrink under GP_POLICY_SHRINK).
   for (int r = 0; r < c->batch; ++r) {
     const int64_t P = c->pages[r];
     if (P < 2) continue;  // flagged on the device if it is asked to compress
     if (P * p.b > 65536) return GP_ERR_UNSUPPORTED;
     const int64_t kq = p.kloc;
     const int64_t loc = (P - 1) * (kq < p.b ? kq : p.b) + (kq < p.b - p.R ? kq : p.b - p.R);
-    if (loc > (P - 1) * p.b - p.R) return GP_ERR_UNSUPPORTED;
+    const int64_t m = (p.policy == GP_POLICY_SHRINK && P >= 3) ? 2 : 1;
+    if (loc > (P - m) * p.b - p.R) return GP_ERR_UNSUPPORTED;
   }
   const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens, c->max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -254,6 +267,12 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
       return gp::launch_compact(p, w, c->batch, action, pool->k_pool, pool->v_pool,
                                 pool->num_pages, bt->block_table, bt->max_pages, bt->num_tokens,
                                 ws, c->d_counters, c->d_err, s);
+    });
+  if (e == hipSuccess && p.policy == GP_POLICY_SHRINK && action)
+    e = timed(c, GP_K_RETURN, s, [&] {
+      return gp::launch_return(c->batch, bt->max_pages, pool->num_pages, bt->block_table,
+                               bt->num_pages, pool->free_stack, pool->free_count, action,
+                               c->d_counters, c->d_err, s);
     });
   return hip_fail(c, e);
 }
@@ -301,13 +320,14 @@ gp_status gp_profile_read(gp_ctx* c, gp_kernel_times* out) {
 
 gp_status gp_get_counters(gp_ctx* c, gp_counters* out) {
   if (!c || !out) return GP_ERR_INVALID_ARG;
-  int64_t h[3];
+  int64_t h[4];
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(h, c->d_counters, sizeof h, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(c, e);
   out->grown = h[0];
   out->compress = h[1];
   out->fallback = h[2];
+  out->shrunk = h[3];
   return GP_OK;
 }
 

@@ -36,6 +36,11 @@ struct Params {
   int L, Hq, Hkv, d, b, R, kloc, p_num, p_den, M;
   double tau;
   float alpha_s, alpha_l;
+  int policy;         // GP_POLICY_*
+  double shrink_tau;  // Shrink threshold (GP_POLICY_SHRINK)
+  int min_tokens;     // Shrink capacity floor
+  // pages of slots one event can free per request: 2 with Shrink, else 1
+  int max_freed() const { return policy == GP_POLICY_SHRINK ? 2 : 1; }
 };
 
 // Workspace layout, identical for gp_demand and gp_compress_hold.
@@ -76,7 +81,7 @@ inline WsLayout ws_layout(const Params& p, int B, int64_t total_tokens, int64_t 
   w.ring_logits = o; o = align256(o + sizeof(float) * (size_t)blocks * max_tokens * kNQ);
   w.ring_keys = o;   o = align256(o + sizeof(float) * (size_t)blocks * max_tokens * 2);
   w.imp = o;         o = align256(o + sizeof(float) * (size_t)w.row_tokens);
-  w.dropped = o;     o = align256(o + sizeof(int32_t) * (size_t)w.rows * p.b);
+  w.dropped = o;     o = align256(o + sizeof(int32_t) * (size_t)w.rows * p.b * p.max_freed());
   w.total = o;
   return w;
 }
@@ -132,6 +137,10 @@ hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* 
                          const int32_t* k_short,
                          const int32_t* k_long, int64_t* k_diff, double* delta,
                          int8_t* decision, hipStream_t s);
+
+hipError_t launch_return(int B, int max_pages, int pool_pages, int32_t* block_table,
+                         int32_t* num_pages, int32_t* free_stack, int32_t* free_count,
+                         const int8_t* action, int64_t* counters, int32_t* err, hipStream_t s);
 
 hipError_t launch_grow(int B, int max_pages, int pool_pages, int32_t* block_table,
                        int32_t* num_pages, const int32_t* free_stack, int32_t* free_count, int reserve,

@@ -5,10 +5,11 @@
 //
 // Kept slots keep their order and move to destination j = slot - #(dropped
 // before slot); for destination j the source is j + #{k : d_k - k <= j},
-// found by binary search over the 256 sorted dropped slots d_k (one search
+// found by binary search over the sorted dropped slots d_k (b of them, 2b for
+// a Shrink row of the GrowPage-Shrink policy, App. H.1) (one search
 // per destination row, kept with both addresses in a per-chunk table).
 // Slots before the first dropped one stay where they are.  Each source lies
-// at most b slots after its destination, so the workgroup walks destinations
+// at most 2b slots after its destination, so the workgroup walks destinations
 // in 512-row chunks (128 KiB, 16 pieces of 16 bytes per thread): it loads a
 // whole chunk into registers, waits for the loads and barriers, then stores.
 // Loads and stores are non-temporal: each byte is touched once, and keeping
@@ -27,7 +28,8 @@ constexpr int kPer = 16;                      // 16-byte pieces per thread per c
 constexpr int kRowsC = kCT * kPer / 16;       // destination rows per chunk (512)
 constexpr int kMaxPages = 65536 / kPage;      // pages per row held in LDS
 
-__global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool_pages,
+__global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stride,
+                                                 int pool_pages,
                                                  const WsHeader* __restrict__ hdr,
                                                  const int64_t* __restrict__ page_off,
                                                  const int8_t* __restrict__ action,
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
                                                  int max_pages, int32_t* __restrict__ num_tokens,
                                                  const int32_t* __restrict__ dropped,
                                                  int32_t* __restrict__ err) {
-  __shared__ int32_t gap[kPage];
+  __shared__ int32_t gap[2 * kPage];
   __shared__ int32_t pg[kMaxPages];
   __shared__ int64_t s_src[2][kRowsC];
   __shared__ int64_t s_dst[2][kRowsC];
@@ -46,14 +48,18 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
   const int LH = L * Hkv;
   const int row = blockIdx.x >> 1, which = blockIdx.x & 1;
   const int r = row / LH, lh = row % LH;
-  if (action && action[r] != GP_COMPRESS) return;
+  const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+  if (act != GP_COMPRESS && act != GP_SHRINK) return;
+  if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
+  const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots freed
+  const int nd = m * b;                    // dropped slots
   const int64_t P = page_off[r + 1] - page_off[r];
-  if (P < 2) return;
+  if (P < m + 1) return;
   const int l = lh / Hkv, h = lh % Hkv;
   const int t = threadIdx.x;
   if (t == 0) bad = 0;
   __syncthreads();
-  for (int k = t; k < kPage; k += kCT) gap[k] = dropped[(int64_t)row * b + k] - k;
+  for (int k = t; k < nd; k += kCT) gap[k] = dropped[(int64_t)row * stride + k] - k;
   for (int i = t; i < P; i += kCT) {
     const int page = block_table[(int64_t)r * max_pages + i];
     if (page < 0 || page >= pool_pages) bad = 1;
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
     return (((int64_t)l * pool_pages + pg[i >> 8]) * Hkv + h) * (int64_t)(kPage * kD) +
            (int64_t)(i & (kPage - 1)) * kD;
   };
-  const int end = (int)((P - 1) * b);
+  const int end = (int)((P - m) * b);
   const int d0 = gap[0] > 0 ? gap[0] : 0;
   int par = 0;
   for (int c0 = d0; c0 < end; c0 += kRowsC, par ^= 1) {
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int pool
     {
       const int drow = c0 + t;
       if (t < kRowsC && drow < end) {
-        int lo = 0, hi = kPage;
+        int lo = 0, hi = nd;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (gap[mid] <= drow) lo = mid + 1; else hi = mid;
@@ -121,7 +127,8 @@ hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_
                           const void* ws, int64_t* counters, int32_t* err, hipStream_t s) {
   const char* base = static_cast<const char*>(ws);
   hipLaunchKernelGGL(k_compact, dim3((unsigned)(w.rows * 2)), dim3(kCT), 0, s, p.L, p.Hkv, p.b,
-                     pool_pages, reinterpret_cast<const WsHeader*>(base + w.header),
+                     p.b * p.max_freed(), pool_pages,
+                     reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), action, k_pool, v_pool,
                      block_table, max_pages, num_tokens,
                      reinterpret_cast<const int32_t*>(base + w.dropped), err);

@@ -12,7 +12,8 @@ namespace gp {
 // Grow iff Delta > tau.  A request of one page has no candidates: Delta = 0
 // and it grows.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau,
+__global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau, int policy,
+                                                double shrink_tau, int min_tokens,
                                                 const WsHeader* __restrict__ hdr,
                                                 const int64_t* __restrict__ page_off,
                                                 const int32_t* __restrict__ k_short,
@@ -46,7 +47,12 @@ __global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau,
     }
     if (k_diff) k_diff[r] = diff;
     if (delta) delta[r] = dl;
-    decision[r] = grow ? GP_GROW : GP_COMPRESS;
+    int8_t dec = grow ? GP_GROW : GP_COMPRESS;
+    // GrowPage-Shrink (App. H.1 Eq. 13): below shrink_tau, and only while
+    // (P - 1) b tokens of capacity, at least min_tokens, would remain
+    if (policy == GP_POLICY_SHRINK && !grow && dl < shrink_tau && (P - 1) * b >= min_tokens)
+      dec = GP_SHRINK;
+    decision[r] = dec;
   }
 }
 
@@ -54,7 +60,8 @@ hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* 
                          const int32_t* k_short, const int32_t* k_long, int64_t* k_diff,
                          double* delta, int8_t* decision, hipStream_t s) {
   const char* base = static_cast<const char*>(ws);
-  hipLaunchKernelGGL(k_decide, dim3(B), dim3(256), 0, s, p.L * p.Hkv, p.b, p.tau,
+  hipLaunchKernelGGL(k_decide, dim3(B), dim3(256), 0, s, p.L * p.Hkv, p.b, p.tau, p.policy,
+                     p.shrink_tau, p.min_tokens,
                      reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), k_short, k_long,
                      k_diff, delta, decision);
@@ -69,6 +76,8 @@ hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* 
 // pages leave the top of the stack in request order.  That is the serial
 // rule computed with one block-wide prefix count.  Everyone else, including
 // growing requests that were refused, is marked for compression.
+// A Shrink decision (GrowPage-Shrink policy) passes through as action
+// GP_SHRINK and takes no page.
 // counters: [0] pages granted, [1] compress actions, [2] fallbacks.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int pool_pages,
@@ -82,9 +91,9 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
                                                     int64_t* __restrict__ counters,
                                                     int32_t* __restrict__ err) {
   __shared__ int scan[kMaxBatch];
-  __shared__ int n_fallback;
+  __shared__ int n_fallback, n_shrink;
   const int t = threadIdx.x;
-  if (t == 0) n_fallback = 0;
+  if (t == 0) n_fallback = n_shrink = 0;
   int fc = *free_count;
   if (fc < 0 || fc > pool_pages) {
     if (t == 0) atomicOr(err, GP_DEVERR_PAGES);
@@ -115,6 +124,9 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
       block_table[(int64_t)t * max_pages + P] = page;
       num_pages[t] = P + 1;
       action[t] = GP_GROW;
+    } else if (decision[t] == GP_SHRINK) {
+      action[t] = GP_SHRINK;  // needs no page; gp_compress_hold returns one
+      atomicAdd(&n_shrink, 1);
     } else {
       action[t] = GP_COMPRESS;
       if (dec_grow) atomicAdd(&n_fallback, 1);
@@ -125,7 +137,7 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
     const int n_grant = total_want < avail ? total_want : avail;
     *free_count = fc - n_grant;
     counters[0] += n_grant;
-    counters[1] += B - n_grant;
+    counters[1] += B - n_grant - n_shrink;
     counters[2] += n_fallback;
   }
 }
@@ -137,6 +149,68 @@ hipError_t launch_grow(int B, int max_pages, int pool_pages, int32_t* block_tabl
   hipLaunchKernelGGL(k_grow, dim3(1), dim3(kMaxBatch), 0, s, B, max_pages, pool_pages,
                      block_table, num_pages, free_stack, free_count, reserve, decision, action,
                      counters, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Shrink's page return (App. H.1: two pages worth of slots are compacted away
+// and one physical page goes back to the global pool).  Runs after the
+// compaction of the event.  Shrinking requests with at least 3 pages are
+// served in index order (block-wide prefix count): the k-th pushes its last
+// page to free_stack[free_count + k], clears that block-table entry and loses
+// one page.  counters[3] counts the pages returned.  A free count outside
+// [0, pool_pages], or a push beyond the stack, flags GP_DEVERR_PAGES and
+// returns nothing.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kMaxBatch) void k_return(int B, int max_pages, int pool_pages,
+                                                      int32_t* __restrict__ block_table,
+                                                      int32_t* __restrict__ num_pages,
+                                                      int32_t* __restrict__ free_stack,
+                                                      int32_t* __restrict__ free_count,
+                                                      const int8_t* __restrict__ action,
+                                                      int64_t* __restrict__ counters,
+                                                      int32_t* __restrict__ err) {
+  __shared__ int scan[kMaxBatch];
+  const int t = threadIdx.x;
+  const int fc = *free_count;
+  int P = 0;
+  bool want = false;
+  if (t < B && action[t] == GP_SHRINK) {
+    P = num_pages[t];
+    want = P >= 3 && P <= max_pages;
+  }
+  scan[t] = want ? 1 : 0;
+  __syncthreads();
+  for (int off = 1; off < kMaxBatch; off <<= 1) {
+    const int add = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  const int total = scan[kMaxBatch - 1];
+  const bool ok = fc >= 0 && fc + total <= pool_pages;
+  if (!ok) {
+    if (t == 0) atomicOr(err, GP_DEVERR_PAGES);
+    return;
+  }
+  if (want) {
+    const int rank = scan[t] - 1;
+    const int64_t at = (int64_t)t * max_pages + (P - 1);
+    free_stack[fc + rank] = block_table[at];
+    block_table[at] = -1;
+    num_pages[t] = P - 1;
+  }
+  if (t == 0) {
+    *free_count = fc + total;
+    counters[3] += total;
+  }
+}
+
+hipError_t launch_return(int B, int max_pages, int pool_pages, int32_t* block_table,
+                         int32_t* num_pages, int32_t* free_stack, int32_t* free_count,
+                         const int8_t* action, int64_t* counters, int32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(k_return, dim3(1), dim3(kMaxBatch), 0, s, B, max_pages, pool_pages,
+                     block_table, num_pages, free_stack, free_count, action, counters, err);
   return hipGetLastError();
 }
 

@@ -3,6 +3,8 @@
 // Reasoning Serving" (arXiv 2609.03494): §3.3 Eq. 9 (importance), Eq. 10
 // (block-local plus global selection), window mask (§3.3, §5.1).
 //
+// A Shrink row (GrowPage-Shrink, App. H.1) drops 2b candidates instead of b
+// (budget (P - 2) b - R); everything below holds with that drop count.
 // Candidates C = [0, N - R): the R newest slots are always kept.  Order:
 // larger importance first, equal importance the newer slot first.  With
 // exactly b candidates to drop per row, the selection is computed from the
@@ -55,17 +57,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
   return base + x - v;
 }
 
-// Steps 2-3: the b smallest candidates of [0, nc) (skipping those marked in
+// Steps 2-3: the nd smallest candidates of [0, nc) (skipping those marked in
 // the S_loc bitmap when PROT), written ascending to dst (and dst2); without
 // PROT each dropped slot is also counted in blkcnt[its block].  Returns the
-// number of candidates the threshold selects (b unless the row is too short).
+// number of candidates the threshold selects (nd unless the row is too short).
 template <bool PROT>
-__device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc, int b,
+__device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc, int nd,
                                              const uint32_t* sloc, uint32_t* hcnt, int* scanbuf,
                                              uint32_t& s_prefix, uint32_t& s_below,
                                              int32_t* dst, int32_t* dst2, int* blkcnt) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  // step 2: value of the b-th smallest unprotected candidate.  Three radix
+  // step 2: value of the nd-th smallest unprotected candidate.  Three radix
   // digits: bits 30..20 (the exponent and three mantissa bits, so that the
   // buckets spread the values and the counting atomics rarely collide), then
   // bits 19..10 and 9..0.  The sign bit is 0 for every importance value.
@@ -82,7 +84,7 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
     }
     __syncthreads();
     if (wv == 0) {
-      // ascending scan: the bucket where the count of smaller values reaches b
+      // ascending scan: the bucket where the count of smaller values reaches nd
       const int per = nb / 64;
       uint32_t lc = 0;
       for (int u = 0; u < per; ++u) lc += hcnt[per * lane + u];
@@ -98,7 +100,7 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
       for (int u = 0; u < per; ++u) {
         const uint32_t before = cum;
         cum += hcnt[per * lane + u];
-        if (best < 0 && cum >= (uint32_t)b) {
+        if (best < 0 && cum >= (uint32_t)nd) {
           best = per * lane + u;
           best_below = before;
         }
@@ -117,7 +119,7 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
     __syncthreads();
   }
   const uint32_t v = prefix;
-  const int need = b - (int)below;
+  const int need = nd - (int)below;
 
   // step 3: ties at v go oldest first; write dropped slots in ascending order
   const int q = (nc + kSel - 1) / kSel;
@@ -128,17 +130,17 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
     if (!(PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) && __float_as_uint(s[i]) == v) ++ties;
   int total;
   const int tie0 = block_excl_scan(ties, scanbuf, &total);
-  int nd = 0;
+  int mine = 0;  // this thread's drops
   {
     int tr = tie0;
     for (int i = lo; i < hi; ++i) {
       if (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) continue;
       const uint32_t key = __float_as_uint(s[i]);
-      if (key < v) ++nd;
-      else if (key == v) nd += (tr++ < need);
+      if (key < v) ++mine;
+      else if (key == v) mine += (tr++ < need);
     }
   }
-  const int pos0 = block_excl_scan(nd, scanbuf, &total);
+  const int pos0 = block_excl_scan(mine, scanbuf, &total);
   {
     int tr = tie0, pos = pos0;
     for (int i = lo; i < hi; ++i) {
@@ -147,7 +149,7 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
       bool drop = key < v;
       if (key == v) drop = tr++ < need;
       if (drop) {
-        if (pos < b) {
+        if (pos < nd) {
           dst[pos] = i;
           if (dst2) dst2[pos] = i;
           if (!PROT) atomicAdd(&blkcnt[i >> 8], 1);
@@ -222,9 +224,9 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 // the answer unless some block would lose more than |B_j| - min(k_loc,
 // |B_j|) of its candidates (then one of them is in that block's protected
 // top), in which case the quotas are computed and the selection repeated
-// over the unprotected candidates.  (The b smallest of C avoid S_loc, so
-// they are also the b smallest of C minus S_loc.)
-__device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int b,
+// over the unprotected candidates.  (The nd smallest of C avoid S_loc, so
+// they are also the nd smallest of C minus S_loc.)
+__device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int nd,
                                            int kloc, uint32_t* sloc, uint32_t* hcnt,
                                            int* scanbuf, int* blkcnt, uint32_t& s_prefix,
                                            uint32_t& s_below, int32_t* dst, int32_t* dst2,
@@ -232,7 +234,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   const int t = threadIdx.x;
   for (int j = t; j < P; j += kSel) blkcnt[j] = 0;
   __syncthreads();
-  int total = drop_smallest<false>(s, nc, b, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
+  int total = drop_smallest<false>(s, nc, nd, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
                                    blkcnt);
   __syncthreads();
   int over = 0;
@@ -245,13 +247,14 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   if (__syncthreads_or(over)) {
     protect_blocks(s, P, nc, kloc, sloc);
     __syncthreads();
-    total = drop_smallest<true>(s, nc, b, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
+    total = drop_smallest<true>(s, nc, nd, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
                                 nullptr);
   }
-  if (t == 0 && total != b) atomicOr(err, GP_DEVERR_SHORT);
+  if (t == 0 && total != nd) atomicOr(err, GP_DEVERR_SHORT);
 }
 
 __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, int kloc,
+                                                 int stride,
                                                  const WsHeader* __restrict__ hdr,
                                                  const int64_t* __restrict__ page_off,
                                                  const int8_t* __restrict__ action,
@@ -269,29 +272,33 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   const int LH = L * Hkv;
   const int row = blockIdx.x;
   const int r = row / LH, lh = row % LH;
-  if (action && action[r] != GP_COMPRESS) return;
+  const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+  if (act != GP_COMPRESS && act != GP_SHRINK) return;
+  if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
+  const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
   const int64_t P = page_off[r + 1] - page_off[r];
   const int t = threadIdx.x;
-  if (P < 2) {
+  if (P < m + 1) {
     if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
     return;
   }
   const int N = (int)(P * b), nc = N - R;
   const int64_t row_tok = (int64_t)LH * page_off[r] * b + (int64_t)lh * N;
   const float* __restrict__ s = imp + row_tok;
-  int32_t* dst = dropped + (int64_t)row * b;
-  int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * b : nullptr;
+  int32_t* dst = dropped + (int64_t)row * stride;
+  int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
+  const int nd = m * b;  // candidates to drop
   if (nc <= kSelLdsTokens) {
     // the row's candidates are read from HBM once, every pass runs on LDS
     const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
     for (int i = t; i < n4; i += kSel)
       reinterpret_cast<float4*>(srow)[i] = reinterpret_cast<const float4*>(s)[i];
     __syncthreads();
-    select_row(srow, (int)P, nc, b, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
+    select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
                dst2, err);
   } else {
-    select_row(s, (int)P, nc, b, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst, dst2,
-               err);
+    select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
+               dst2, err);
   }
 }
 
@@ -299,7 +306,8 @@ hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t
                          void* ws, int32_t* dropped_out, int32_t* err, hipStream_t s) {
   char* base = static_cast<char*>(ws);
   hipLaunchKernelGGL(k_select, dim3((unsigned)w.rows), dim3(kSel), 0, s, p.L, p.Hkv, p.b, p.R,
-                     p.kloc, reinterpret_cast<const WsHeader*>(base + w.header),
+                     p.kloc, p.b * p.max_freed(),
+                     reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), action,
                      reinterpret_cast<const float*>(base + w.imp),
                      reinterpret_cast<int32_t*>(base + w.dropped), dropped_out, err);

@@ -32,7 +32,8 @@ class BoundaryRunner:
                               device=dev)
         self.out = gb.DemandOut.empty(cfg, B, dev, row_tokens if want_abar else None)
         self.action = torch.empty(B, dtype=torch.int8, device=dev)
-        self.dropped = (torch.full((B, cfg.num_layers, cfg.num_kv_heads, cfg.page_size), -1,
+        self.dropped = (torch.full((B, cfg.num_layers, cfg.num_kv_heads,
+                                    cfg.page_size * cfg.max_freed), -1,
                                    dtype=torch.int32, device=dev) if want_dropped else None)
 
     def update(self, q: torch.Tensor, first_step: torch.Tensor, stream=None):

@@ -24,7 +24,8 @@ def oracle_config(cfg: gb.Config) -> OracleConfig:
     return OracleConfig(L=cfg.num_layers, Hq=cfg.num_q_heads, Hkv=cfg.num_kv_heads,
                         d=cfg.head_dim, b=cfg.page_size, R=cfg.recent_window,
                         k_loc=cfg.local_quota, p_num=cfg.p_num, p_den=cfg.p_den, tau=cfg.tau,
-                        alpha_s=cfg.alpha_short, alpha_l=cfg.alpha_long, M=cfg.max_slots)
+                        alpha_s=cfg.alpha_short, alpha_l=cfg.alpha_long, M=cfg.max_slots,
+                        policy=cfg.policy, shrink_tau=cfg.shrink_tau, min_tokens=cfg.min_tokens)
 
 
 def bf16_np(t: torch.Tensor) -> np.ndarray:
@@ -112,13 +113,16 @@ def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
     B = len(P)
     dropped = {}
     compacted = {}
+    freed = np.zeros(B, np.int32)  # pages of slots each request frees
     for r in range(B):
-        if action[r] != oracle.COMPRESS or hc.P[r] < 2:
+        m = {oracle.COMPRESS: 1, oracle.SHRINK: 2}.get(int(action[r]), 0)
+        if m == 0 or hc.P[r] < m + 1:
             continue
+        freed[r] = m
         pages = hc.bt[r, :hc.P[r]]
         for l in range(ocfg.L):
             for h in range(ocfg.Hkv):
-                keep = oracle.select(ocfg, dem["abar"][(r, l, h)])
+                keep = oracle.select(ocfg, dem["abar"][(r, l, h)], pages=m)
                 N = keep.size
                 dropped[(r, l, h)] = np.nonzero(keep[:N - ocfg.R] == 0)[0].astype(np.int32)
                 ks = hc.keys(l, h, pages)
@@ -126,8 +130,11 @@ def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
                 n = oracle.compact(ks, keep)
                 oracle.compact(vs, keep)
                 compacted[(r, l, h)] = (ks[:n], vs[:n])
+    stack = hc.free_stack.copy()
+    shrunk, fc = oracle.return_pages(action, bt, P, stack, fc)
     return dict(dem=dem, action=action, bt=bt, P=P, free_count=fc, counters=counters,
-                dropped=dropped, compacted=compacted)
+                dropped=dropped, compacted=compacted, freed=freed, free_stack=stack,
+                shrunk=shrunk)
 
 
 def row_offsets(P: np.ndarray, L: int, Hkv: int, b: int):

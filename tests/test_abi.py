@@ -38,4 +38,34 @@ def test_status_strings_and_invalid_config():
     assert lib.gp_create(ctypes.byref(bad2), ctypes.byref(h)) == 1
     bad3 = gb.gp_config(2, 8, 2, 128, 256, 16, 64, 101, 100, 0.0, 0.1, 0.001, 8)  # p > 1
     assert lib.gp_create(ctypes.byref(bad3), ctypes.byref(h)) == 1
+    bad4 = gb.gp_config(2, 8, 2, 128, 256, 16, 64, 99, 100, 0.0, 0.1, 0.001, 8, 7, -0.005, 1024)
+    assert lib.gp_create(ctypes.byref(bad4), ctypes.byref(h)) == 1  # unknown policy
+    bad5 = gb.gp_config(2, 8, 2, 128, 256, 16, 64, 99, 100, 0.0, 0.1, 0.001, 8, 1, 0.01, 1024)
+    assert lib.gp_create(ctypes.byref(bad5), ctypes.byref(h)) == 1  # shrink_tau > tau
     assert not h.value
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structures have the sizes and field offsets the C
+    compiler gives the header's structs."""
+    structs = {"gp_config": gb.gp_config, "gp_pool": gb.gp_pool, "gp_batch": gb.gp_batch,
+               "gp_demand_out": gb.gp_demand_out, "gp_counters": gb.gp_counters,
+               "gp_kernel_times": gb.gp_kernel_times}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "growpage.h"', 'int main(void) {']
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines.append('  return 0;\n}')
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                  text=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, (name, f)

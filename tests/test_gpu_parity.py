@@ -109,6 +109,51 @@ def test_max_batch_1024_requests():
 
 
 @needs_gpu
+def test_shrink_policy_batch():
+    """GrowPage-Shrink (App. H.1 Eq. 13): a batch whose decisions cover all
+    three actions (Shrink where Delta < -0.005 and at least 1024 tokens of
+    capacity remain, Compress & Hold for a request below that floor and for
+    Grow decisions that find no page, Grow otherwise); against the oracle:
+    decisions, grants, the 2b dropped slots and compacted bytes of shrinking
+    rows, the returned pages on the free stack, block tables, page counts and
+    counters."""
+    log("test_shrink_policy_batch")
+    P = [6, 5, 7, 4, 3, 8, 5]
+    align = ["S", "S", "L", "S", "L", None, "L"]
+    wl = synth.make_workload(SMALL, P, 64, seed=4242, device="cuda", align=align,
+                             cluster_sizes=[30, 60, 30, 30, 30, 30, 30], free_pages=2,
+                             steps=120, short_steps=16, max_slots=8)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots, policy=1)
+    ref = check_event(wl, cfg, check_f64=False)
+    act = list(ref["action"])
+    log(f"  actions {act}, decisions {list(ref['dem']['decision'])}")
+    assert act.count(2) >= 2 and act[3] == 0  # P = 4 is at the capacity floor
+    assert ref["shrunk"] == act.count(2)
+
+
+@needs_gpu
+def test_shrink_ignored_under_default_policy():
+    """A caller-forced GP_SHRINK action under the default policy changes
+    nothing (the workspace holds one page of drops per row)."""
+    log("test_shrink_ignored_under_default_policy")
+    wl = synth.make_workload(SMALL, [6, 5], 24, seed=4243, device="cuda", align=["S", "S"],
+                             cluster_sizes=[30, 30], free_pages=0, steps=60, short_steps=8,
+                             max_slots=4)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    bt0 = wl.block_table.clone()
+    nt0 = wl.num_tokens.clone()
+    k0 = device_rows(wl.k_pool, 1, 0, wl.block_table[0, :6].cpu().numpy())
+    run.demand(q)
+    run.compress(action=torch.full((2,), 2, dtype=torch.int8, device="cuda"))
+    torch.cuda.synchronize()
+    assert run.device_errors() == 0
+    assert torch.equal(wl.block_table, bt0) and torch.equal(wl.num_tokens, nt0)
+    assert np.array_equal(device_rows(wl.k_pool, 1, 0, wl.block_table[0, :6].cpu().numpy()), k0)
+
+
+@needs_gpu
 def test_junk_page_needs_block_quota():
     """One logical page of request 0 holds keys pointing away from both
     summary directions in every (layer, KV head): their attention underflows
@@ -148,6 +193,20 @@ def test_quota_and_reserve(k_loc, reserve):
                              free_pages=2, steps=120, short_steps=16, max_slots=8)
     cfg = gb_config(wl.shape, max_slots=wl.max_slots, local_quota=k_loc)
     check_event(wl, cfg, reserve=reserve)
+
+
+@needs_gpu
+def test_llama8k_shrink_full_size():
+    """Llama-8B shape at full size (8192 tokens, 4096-page pool) under the
+    Shrink policy, clusters on the short view: the request shrinks (2b slots
+    dropped per row, one page returned), every row compared with the oracle."""
+    log("test_llama8k_shrink_full_size")
+    wl = synth.llama8k("compress", "cuda")
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots, policy=1)
+    ref = check_event(wl, cfg, check_f64=False)
+    assert ref["action"][0] == 2 and ref["shrunk"] == 1
+    del wl
+    torch.cuda.empty_cache()
 
 
 @needs_gpu

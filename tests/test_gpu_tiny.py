@@ -94,20 +94,25 @@ def check_event(wl, cfg, reserve=0, check_f64=True):
     assert int(wl.free_count.item()) == ref["free_count"]
     c = run.counters()
     assert [c["grown"], c["compress"], c["fallback"]] == list(ref["counters"])
+    assert c["shrunk"] == ref["shrunk"]
+    if cfg.policy == 1:
+        np.testing.assert_array_equal(wl.free_stack.cpu().numpy()[:ref["free_count"]],
+                                      ref["free_stack"][:ref["free_count"]])
     # compress: dropped slots, compacted bytes, token counts
     dropped = run.dropped.cpu().numpy()
     nt = run.batch.num_tokens.cpu().numpy()
     for r in range(len(hc.P)):
         N = int(hc.P[r]) * ocfg.b
         pages = hc.bt[r, :hc.P[r]]
-        if ref["action"][r] == oracle.COMPRESS and hc.P[r] >= 2:
-            assert nt[r] == N - ocfg.b
+        m = int(ref["freed"][r])
+        if m > 0:
+            assert nt[r] == N - m * ocfg.b
             for l in range(ocfg.L):
                 for h in range(ocfg.Hkv):
-                    assert np.array_equal(dropped[r, l, h], ref["dropped"][(r, l, h)])
+                    assert np.array_equal(dropped[r, l, h, :m * ocfg.b], ref["dropped"][(r, l, h)])
                     kw, vw = ref["compacted"][(r, l, h)]
-                    kg = device_rows(wl.k_pool, l, h, pages)[:N - ocfg.b]
-                    vg = device_rows(wl.v_pool, l, h, pages)[:N - ocfg.b]
+                    kg = device_rows(wl.k_pool, l, h, pages)[:N - m * ocfg.b]
+                    vg = device_rows(wl.v_pool, l, h, pages)[:N - m * ocfg.b]
                     assert np.array_equal(kg, kw) and np.array_equal(vg, vw), (r, l, h)
         else:
             assert nt[r] == N
