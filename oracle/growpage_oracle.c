@@ -454,24 +454,94 @@ int orc_select(const float* abar_all, int N, int b, int R, int k_loc,
  * the global pool.  Requests are served in index order, each pushing its
  * page on top of the free stack (so a later Grow takes the most recently
  * returned page first); the block-table entry is cleared to -1 and P
- * decreases by one.  Requests with fewer than 3 pages are left alone.
- * Returns the number of pages returned.
- * Pins: pool arithmetic and order.
+ * decreases by one.  Requests with fewer than 3 pages are left alone.  With
+ * reference counts (refcount != NULL, Appendix E.2) a last page that other
+ * requests still reference is not pushed: the request only drops its
+ * reference (refcount - 1).  Returns the number of pages pushed.
+ * Pins: pool arithmetic and order, shared last pages.
  * ---------------------------------------------------------------------- */
 int orc_return_pages(const int8_t* action, int B, int32_t* block_table,
                      int max_pages, int32_t* num_pages, int32_t* free_stack,
-                     int32_t* free_count) {
+                     int32_t* free_count, int32_t* refcount) {
   int n = 0;
   for (int r = 0; r < B; ++r) {
     if (action[r] != ORC_SHRINK || num_pages[r] < 3) continue;
     const size_t at = (size_t)r * max_pages + (num_pages[r] - 1);
-    free_stack[*free_count] = block_table[at];
-    *free_count += 1;
+    const int32_t page = block_table[at];
+    if (refcount && refcount[page] > 1) {
+      refcount[page] -= 1;
+    } else {
+      free_stack[*free_count] = page;
+      *free_count += 1;
+      if (refcount) refcount[page] = 0;
+      ++n;
+    }
     block_table[at] = -1;
     num_pages[r] -= 1;
-    ++n;
   }
   return n;
+}
+
+/* ------------------------------------------------------------------------
+ * Prefix-cache-aware compression (Appendix E.2): a page referenced by more
+ * than one request (refcount > 1) is never written by a request's
+ * compression.  Each compressing request (action Compress & Hold or
+ * Shrink) gets a new target page for every shared page it keeps: pages
+ * 0 .. P-1 for Compress & Hold (the last page's slots are written by later
+ * decoding), 0 .. P-2 for Shrink (its last page is released by
+ * orc_return_pages).  Requests are served in index order from the top of
+ * the free stack; a request whose pages cannot all be allocated, and every
+ * later request that needs any, is not compressed (ok[r] = 0, its action
+ * left to the caller: it is skipped).  target[r][i] = new page, or -1 to
+ * keep page i.  Returns the number of pages allocated.
+ * Pins: allocation order and counts, the all-or-nothing prefix rule.
+ * ---------------------------------------------------------------------- */
+int orc_share_plan(const int8_t* action, int B, const int32_t* block_table,
+                   int max_pages, const int32_t* num_pages, const int32_t* refcount,
+                   const int32_t* free_stack, int32_t* free_count, int32_t* target,
+                   uint8_t* ok) {
+  int used = 0;
+  int blocked = 0;
+  for (int r = 0; r < B; ++r) {
+    for (int i = 0; i < max_pages; ++i) target[(size_t)r * max_pages + i] = -1;
+    ok[r] = 1;
+    const int m = action[r] == ORC_COMPRESS ? 1 : (action[r] == ORC_SHRINK ? 2 : 0);
+    if (m == 0 || num_pages[r] < m + 1) continue;
+    const int keep_pages = m == 1 ? num_pages[r] : num_pages[r] - 1;
+    int need = 0;
+    for (int i = 0; i < keep_pages; ++i)
+      need += refcount[block_table[(size_t)r * max_pages + i]] > 1;
+    if (need == 0) continue;
+    if (blocked || used + need > *free_count) {
+      blocked = 1;
+      ok[r] = 0;
+      continue;
+    }
+    for (int i = 0; i < keep_pages; ++i)
+      if (refcount[block_table[(size_t)r * max_pages + i]] > 1)
+        target[(size_t)r * max_pages + i] = free_stack[*free_count - 1 - used++];
+  }
+  *free_count -= used;
+  return used;
+}
+
+/* After the compaction of the event: every replaced page of a served request
+ * is swapped in its block table for its target; the request drops its
+ * reference to the old page (refcount - 1) and owns the new one
+ * (refcount 1).  Appendix E.2. */
+void orc_share_release(int B, int32_t* block_table, int max_pages, const int32_t* target,
+                       const uint8_t* ok, int32_t* refcount) {
+  for (int r = 0; r < B; ++r) {
+    if (!ok[r]) continue;
+    for (int i = 0; i < max_pages; ++i) {
+      const int32_t t = target[(size_t)r * max_pages + i];
+      if (t < 0) continue;
+      const size_t at = (size_t)r * max_pages + i;
+      refcount[block_table[at]] -= 1;
+      refcount[t] = 1;
+      block_table[at] = t;
+    }
+  }
 }
 
 /* ------------------------------------------------------------------------

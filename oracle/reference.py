@@ -67,8 +67,12 @@ def lib():
         L.orc_decide_shrink.argtypes = [i32p, i32p, c_int, ctypes.c_int64, c_int, c_int, c_double,
                                         c_double, c_int, i64p, ctypes.POINTER(c_double)]
         L.orc_decide_shrink.restype = c_int
-        L.orc_return_pages.argtypes = [i8p, c_int, i32p, c_int, i32p, i32p, i32p]
+        L.orc_return_pages.argtypes = [i8p, c_int, i32p, c_int, i32p, i32p, i32p, i32p]
         L.orc_return_pages.restype = c_int
+        L.orc_share_plan.argtypes = [i8p, c_int, i32p, c_int, i32p, i32p, i32p, i32p, i32p, u8p]
+        L.orc_share_plan.restype = c_int
+        L.orc_share_release.argtypes = [c_int, i32p, c_int, i32p, u8p, i32p]
+        L.orc_share_release.restype = None
         L.orc_compact.argtypes = [u16p, u8p, c_int, c_int]
         L.orc_compact.restype = c_int
         _LIB = L
@@ -226,18 +230,53 @@ def select(cfg: OracleConfig, abar_all: np.ndarray, k_loc: int | None = None,
 
 
 def return_pages(action: np.ndarray, block_table: np.ndarray, num_pages: np.ndarray,
-                 free_stack: np.ndarray, free_count: int):
+                 free_stack: np.ndarray, free_count: int, refcount: np.ndarray | None = None):
     """Shrink's page return, in place on block_table / num_pages /
-    free_stack.  Returns (pages returned, free_count)."""
+    free_stack (and refcount).  Returns (pages pushed, free_count)."""
     action = np.ascontiguousarray(action, dtype=np.int8)
     B, max_pages = block_table.shape
     assert block_table.dtype == np.int32 and num_pages.dtype == np.int32
     assert free_stack.dtype == np.int32 and free_stack.flags["C_CONTIGUOUS"]
     fc = np.array([free_count], dtype=np.int32)
+    rc = ctypes.POINTER(ctypes.c_int32)()
+    if refcount is not None:
+        assert refcount.dtype == np.int32 and refcount.flags["C_CONTIGUOUS"]
+        rc = _p(refcount, ctypes.c_int32)
     n = lib().orc_return_pages(_p(action, ctypes.c_int8), B, _p(block_table, ctypes.c_int32),
                                max_pages, _p(num_pages, ctypes.c_int32),
-                               _p(free_stack, ctypes.c_int32), _p(fc, ctypes.c_int32))
+                               _p(free_stack, ctypes.c_int32), _p(fc, ctypes.c_int32), rc)
     return int(n), int(fc[0])
+
+
+def share_plan(action: np.ndarray, block_table: np.ndarray, num_pages: np.ndarray,
+               refcount: np.ndarray, free_stack: np.ndarray, free_count: int):
+    """Target pages of prefix-cache-aware compression (Appendix E.2).
+    Returns (target [B][max_pages], ok [B], pages allocated, free_count)."""
+    action = np.ascontiguousarray(action, dtype=np.int8)
+    B, max_pages = block_table.shape
+    target = np.empty((B, max_pages), np.int32)
+    ok = np.empty(B, np.uint8)
+    fc = np.array([free_count], dtype=np.int32)
+    used = lib().orc_share_plan(_p(action, ctypes.c_int8), B,
+                                _p(np.ascontiguousarray(block_table, np.int32), ctypes.c_int32),
+                                max_pages,
+                                _p(np.ascontiguousarray(num_pages, np.int32), ctypes.c_int32),
+                                _p(np.ascontiguousarray(refcount, np.int32), ctypes.c_int32),
+                                _p(np.ascontiguousarray(free_stack, np.int32), ctypes.c_int32),
+                                _p(fc, ctypes.c_int32), _p(target, ctypes.c_int32),
+                                _p(ok, ctypes.c_uint8))
+    return target, ok, int(used), int(fc[0])
+
+
+def share_release(block_table: np.ndarray, target: np.ndarray, ok: np.ndarray,
+                  refcount: np.ndarray) -> None:
+    """Swap replaced pages for their targets and move the references, in place."""
+    B, max_pages = block_table.shape
+    assert block_table.dtype == np.int32 and refcount.dtype == np.int32
+    lib().orc_share_release(B, _p(block_table, ctypes.c_int32), max_pages,
+                            _p(np.ascontiguousarray(target, np.int32), ctypes.c_int32),
+                            _p(np.ascontiguousarray(ok, np.uint8), ctypes.c_uint8),
+                            _p(refcount, ctypes.c_int32))
 
 
 def compact(rows: np.ndarray, keep: np.ndarray) -> int:

@@ -387,6 +387,60 @@ def test_return_pages_pool_arithmetic():
     assert list(P) == [4, 4, 2, 5, 3]
 
 
+def test_share_plan_allocation_order_and_prefix_rule():
+    """orc_share_plan (Appendix E.2): a compressing request gets a new target
+    page for every shared page it keeps (all P for Compress & Hold, the first
+    P - 1 for Shrink), from the top of the free stack in request and page
+    order; once one request cannot get all its pages, no later request that
+    needs any is served."""
+    B, maxp = 4, 6
+    bt = np.array([[100, 101, 102, 103, -1, -1],
+                   [110, 111, 112, -1, -1, -1],
+                   [120, 121, 122, 123, 124, -1],
+                   [130, 131, 132, -1, -1, -1]], np.int32)
+    P = np.array([4, 3, 5, 3], np.int32)
+    action = np.array([0, 1, 2, 0], np.int8)  # C&H, Grow, Shrink, C&H
+    rc = np.ones(200, np.int32)
+    rc[[100, 102, 111, 121, 124, 132]] = 2     # shared pages
+    stack = np.array([10, 11, 12, 13], np.int32)
+    target, ok, used, fc = oracle.share_plan(action, bt, P, rc, stack, 4)
+    assert used == 4 and fc == 0 and list(ok) == [1, 1, 1, 1]
+    assert target[0, 0] == 13 and target[0, 2] == 12 and target[2, 1] == 11 and target[3, 2] == 10
+    assert (target >= 0).sum() == 4  # the Grow request and Shrink's last page are not replaced
+    target, ok, used, fc = oracle.share_plan(action, bt, P, rc, stack, 3)
+    assert list(ok) == [1, 1, 1, 0] and used == 3 and fc == 0
+    target, ok, used, fc = oracle.share_plan(action, bt, P, rc, stack, 1)
+    assert list(ok) == [0, 1, 0, 0] and used == 0 and fc == 1 and (target >= 0).sum() == 0
+
+
+def test_share_release_moves_references():
+    """orc_share_release (Appendix E.2): replaced pages are swapped for their
+    targets; the old page loses one reference, the new one has one."""
+    bt = np.array([[100, 101, 102]], np.int32)
+    target = np.array([[7, -1, 9]], np.int32)
+    rc = np.ones(200, np.int32)
+    rc[[100, 102]] = 3
+    rc[[7, 9]] = 0
+    oracle.share_release(bt, target, np.array([1], np.uint8), rc)
+    assert list(bt[0]) == [7, 101, 9] and rc[100] == 2 and rc[102] == 2 and rc[7] == 1 and rc[9] == 1
+    bt2 = np.array([[100, 101, 102]], np.int32)
+    oracle.share_release(bt2, target, np.array([0], np.uint8), rc)  # a skipped request
+    assert list(bt2[0]) == [100, 101, 102] and rc[100] == 2
+
+
+def test_return_pages_shared_last_page():
+    """With reference counts, a shrinking request whose last page is shared
+    drops its reference instead of pushing the page on the free stack."""
+    bt = np.array([[1, 2, 3, 4], [5, 6, 7, 8]], np.int32)
+    P = np.array([4, 4], np.int32)
+    rc = np.ones(10, np.int32)
+    rc[4] = 2
+    stack = np.zeros(6, np.int32)
+    n, fc = oracle.return_pages(np.array([2, 2], np.int8), bt, P, stack, 0, refcount=rc)
+    assert n == 1 and fc == 1 and stack[0] == 8 and rc[4] == 1 and rc[8] == 0
+    assert list(bt[:, 3]) == [-1, -1] and list(P) == [3, 3]
+
+
 # ------------------------------------------------------------------ grow --
 
 def test_grow_pool_arithmetic_and_fallback():
