@@ -64,7 +64,9 @@ enum gp_err_bits {
   GP_DEVERR_POSITION = 2,  /* position outside [0, rope_rows): clamped */
   GP_DEVERR_PAGE = 4,      /* page id outside [0, num_pages): tile skipped */
   GP_DEVERR_SHORT = 8,     /* compress requested with fewer than 2 pages */
-  GP_DEVERR_PAGES = 16     /* device page count outside [1, max_pages] */
+  GP_DEVERR_PAGES = 16,    /* device page count outside [1, max_pages] */
+  GP_DEVERR_NOPAGE = 32    /* no free pages to replace a compressing request's
+                              shared pages (App. E.2): request left uncompressed */
 };
 
 /* Actions and decisions (int8 on the device). */
@@ -104,6 +106,8 @@ typedef struct gp_pool {
   int32_t num_pages;    /* pages in the pool */
   int32_t* free_stack;  /* device int32 [num_pages]; free ids in [0, free_count) */
   int32_t* free_count;  /* device int32 [1]; top of stack is free_stack[free_count - 1] */
+  int32_t* refcount;    /* device int32 [num_pages] references per page (prefix sharing,
+                           App. E.2), or NULL: every page referenced once */
 } gp_pool;
 
 /* A batch of requests at their capacity boundary (N = P * b for each). */
@@ -139,6 +143,7 @@ typedef struct gp_counters {
   int64_t compress;  /* Compress & Hold actions (decisions plus fallbacks) */
   int64_t fallback;  /* Grow decisions that fell back (§4.2, App. H.2) */
   int64_t shrunk;    /* pages returned to the pool by Shrink (App. H.1) */
+  int64_t copied;    /* target pages allocated to replace shared pages (App. E.2) */
 } gp_counters;
 
 typedef struct gp_ctx gp_ctx;
@@ -185,7 +190,8 @@ gp_status gp_demand(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
 /* A6: Grow by One Page with fallback (§3.3; §4.2; App. H.2).  Requests are
  * served in index order: a request whose decision is GP_GROW takes the page on
  * top of the free stack while more than reserve_pages are free and its block
- * table has room; the page is appended to its block table and P += 1.
+ * table has room; the page is appended to its block table and P += 1 (with
+ * reference counts, the page gets one reference).
  * Otherwise it falls back to compression.  action[b] receives GP_GROW or
  * GP_COMPRESS, or GP_SHRINK for a GP_SHRINK decision (no page is taken);
  * decision may come from gp_demand or from the caller (policy variants).
@@ -208,7 +214,22 @@ gp_status gp_grow_page(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
  * page is pushed on the free stack (requests in index order), its block-table
  * entry set to -1, P -= 1 and num_tokens = (P-2) b with the old P; a Shrink
  * with fewer than 3 pages sets GP_DEVERR_SHORT and leaves the request as it
- * was; under GP_POLICY_GROWPAGE a GP_SHRINK action is ignored.  Must follow gp_demand on the same batch with the same workspace.
+ * was; under GP_POLICY_GROWPAGE a GP_SHRINK action is ignored.
+ * Prefix sharing (App. E.2; pool->refcount != NULL): a page with more than
+ * one reference is never written.  Before selection, each compressing
+ * request gets a new target page for every shared page it keeps (its P
+ * pages, or its first P-1 for Shrink), from the top of the free stack in
+ * request and page order; a request whose pages cannot all be allocated, and
+ * every later one that needs any, is left uncompressed (GP_DEVERR_NOPAGE).
+ * The compaction writes the kept rows of a replaced page into its target
+ * (copying rows before the first drop too); afterwards the block table
+ * points at the targets, the old pages lose one reference each and the
+ * targets have one; a page whose count reaches zero is left to the caller
+ * (a prefix cache keeps it until eviction).  A Shrink whose last page is
+ * shared drops its reference instead of returning the page, which goes back
+ * to the pool with its last reference (requests in index order).  Counts
+ * must be at least the number of block-table references to each page.
+ * Must follow gp_demand on the same batch with the same workspace.
  * dropped_out (optional, device int32 [B][L][Hkv][b] under
  * GP_POLICY_GROWPAGE, [B][L][Hkv][2b] under GP_POLICY_SHRINK) receives the
  * dropped slots in ascending order; rows of requests that do not compress
@@ -228,8 +249,10 @@ enum gp_kernel_id {
   GP_K_GROW = 5,    /* A6 page grant and fallback */
   GP_K_SELECT = 6,  /* A7-A8 window mask and Eq. 10 selection */
   GP_K_COMPACT = 7, /* A9 in-place compaction */
-  GP_K_RETURN = 8,  /* Shrink's page return (GP_POLICY_SHRINK only) */
-  GP_NUM_KERNELS = 9
+  GP_K_RETURN = 8,  /* page bookkeeping after compaction: shared-page release, Shrink's
+                       page return (prefix sharing or GP_POLICY_SHRINK only) */
+  GP_K_SHARE = 9,   /* target pages for shared pages (prefix sharing only) */
+  GP_NUM_KERNELS = 10
 };
 
 typedef struct gp_kernel_times {

@@ -198,8 +198,11 @@ def decide(cfg: OracleConfig, ks: np.ndarray, kl: np.ndarray, card_c: int,
 
 
 def grow(decision: np.ndarray, block_table: np.ndarray, num_pages: np.ndarray,
-         free_stack: np.ndarray, free_count: int, reserve: int = 0):
-    """A6 in place on block_table / num_pages.  Returns (action, free_count, counters)."""
+         free_stack: np.ndarray, free_count: int, reserve: int = 0,
+         refcount: np.ndarray | None = None):
+    """A6 in place on block_table / num_pages.  Returns (action, free_count, counters).
+    With reference counts (App. E.2: Grow by One Page appends a page that only
+    this request references), each granted page gets a count of 1."""
     decision = np.ascontiguousarray(decision, dtype=np.int8)
     B, max_pages = block_table.shape
     assert block_table.dtype == np.int32 and num_pages.dtype == np.int32
@@ -210,6 +213,9 @@ def grow(decision: np.ndarray, block_table: np.ndarray, num_pages: np.ndarray,
     lib().orc_grow(_p(decision, ctypes.c_int8), B, _p(block_table, ctypes.c_int32), max_pages,
                    _p(num_pages, ctypes.c_int32), _p(fs, ctypes.c_int32), _p(fc, ctypes.c_int32),
                    int(reserve), _p(action, ctypes.c_int8), _p(counters, ctypes.c_int64))
+    if refcount is not None:
+        for r in np.nonzero(action == GROW)[0]:
+            refcount[block_table[r, num_pages[r] - 1]] = 1
     return action, int(fc[0]), counters
 
 

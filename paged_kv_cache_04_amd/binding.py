@@ -28,7 +28,8 @@ SYMBOLS = (
     "gp_status_str", "gp_last_hip_error", "gp_profile", "gp_profile_read",
 )
 
-KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact", "return")
+KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact", "return",
+           "share")
 
 
 class GPError(RuntimeError):
@@ -52,6 +53,7 @@ class gp_pool(ctypes.Structure):
     _fields_ = [
         ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("num_pages", ctypes.c_int32),
         ("free_stack", ctypes.c_void_p), ("free_count", ctypes.c_void_p),
+        ("refcount", ctypes.c_void_p),
     ]
 
 
@@ -77,7 +79,8 @@ class gp_kernel_times(ctypes.Structure):
 
 class gp_counters(ctypes.Structure):
     _fields_ = [("grown", ctypes.c_int64), ("compress", ctypes.c_int64),
-                ("fallback", ctypes.c_int64), ("shrunk", ctypes.c_int64)]
+                ("fallback", ctypes.c_int64), ("shrunk", ctypes.c_int64),
+                ("copied", ctypes.c_int64)]
 
 
 _lib = None
@@ -208,10 +211,11 @@ class Pool:
     v_pool: torch.Tensor
     free_stack: torch.Tensor  # int32 [num_pages]
     free_count: torch.Tensor  # int32 [1]
+    refcount: torch.Tensor | None = None  # int32 [num_pages], prefix sharing
 
     def c(self) -> gp_pool:
         return gp_pool(_ptr(self.k_pool), _ptr(self.v_pool), int(self.k_pool.shape[1]),
-                       _ptr(self.free_stack), _ptr(self.free_count))
+                       _ptr(self.free_stack), _ptr(self.free_count), _ptr(self.refcount))
 
 
 @dataclass
@@ -293,7 +297,8 @@ def gp_compress_hold(ctx: Context, pool: Pool, batch: Batch, action, workspace,
 def gp_get_counters(ctx: Context) -> dict:
     c = gp_counters()
     _check(load().gp_get_counters(ctx.handle, ctypes.byref(c)), "gp_get_counters", ctx)
-    return dict(grown=c.grown, compress=c.compress, fallback=c.fallback, shrunk=c.shrunk)
+    return dict(grown=c.grown, compress=c.compress, fallback=c.fallback, shrunk=c.shrunk,
+                copied=c.copied)
 
 
 def gp_get_device_errors(ctx: Context) -> int:

@@ -12,7 +12,7 @@ struct gp_ctx {
   gp::Params p;
   int device = 0;
   int num_cus = 256;
-  int64_t* d_counters = nullptr;  // [4]: granted, compress, fallback, returned
+  int64_t* d_counters = nullptr;  // [5]: granted, compress, fallback, returned, copied
   int32_t* d_err = nullptr;       // [1], right after the counters
   int last_hip = 0;
   // bookkeeping of the last gp_demand, checked by gp_compress_hold
@@ -133,7 +133,7 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
     delete c;
     return GP_ERR_HIP;
   }
-  c->d_err = reinterpret_cast<int32_t*>(c->d_counters + 4);
+  c->d_err = reinterpret_cast<int32_t*>(c->d_counters + 5);
   *out = c;
   return GP_OK;
 }
@@ -228,7 +228,7 @@ gp_status gp_grow_page(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   return hip_fail(c, timed(c, GP_K_GROW, s, [&] {
     return gp::launch_grow(bt->batch, bt->max_pages, pool->num_pages, bt->block_table,
                            bt->num_pages, pool->free_stack, pool->free_count, reserve_pages,
-                           decision, action, c->d_counters, c->d_err, s);
+                           decision, action, pool->refcount, c->d_counters, c->d_err, s);
   }));
 }
 
@@ -242,8 +242,9 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   if (!ws || ws != c->ws || ws_bytes != c->ws_bytes || bt->batch != c->batch)
     return GP_ERR_WORKSPACE;
   const gp::Params& p = c->p;
-  if (p.policy == GP_POLICY_SHRINK && action &&
-      (!pool->free_stack || !pool->free_count || !bt->num_pages || pool->num_pages < 1))
+  const bool shrink = p.policy == GP_POLICY_SHRINK && action;
+  const bool shared = pool->refcount != nullptr;
+  if ((shrink || shared) && (!pool->free_stack || !pool->free_count || !bt->num_pages))
     return GP_ERR_INVALID_ARG;
   // Eq. 10 needs the local quotas to fit the budget K_t = (P - m) b - R,
   // m = 1 for Compress & Hold, 2 for Shrink (any request with 3 or more pages
@@ -259,20 +260,26 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   }
   const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens, c->max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = timed(c, GP_K_SELECT, s, [&] {
-    return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);
+  hipError_t e = timed(c, GP_K_SHARE, s, [&] {
+    return gp::launch_share(p, w, c->batch, action, pool->num_pages, bt->block_table,
+                            bt->max_pages, pool->refcount, pool->free_stack, pool->free_count, ws,
+                            c->d_counters, c->d_err, s);
   });
+  if (e == hipSuccess)
+    e = timed(c, GP_K_SELECT, s, [&] {
+      return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);
+    });
   if (e == hipSuccess)
     e = timed(c, GP_K_COMPACT, s, [&] {
       return gp::launch_compact(p, w, c->batch, action, pool->k_pool, pool->v_pool,
                                 pool->num_pages, bt->block_table, bt->max_pages, bt->num_tokens,
-                                ws, c->d_counters, c->d_err, s);
+                                shared, ws, c->d_err, s);
     });
-  if (e == hipSuccess && p.policy == GP_POLICY_SHRINK && action)
+  if (e == hipSuccess && (shrink || shared))
     e = timed(c, GP_K_RETURN, s, [&] {
-      return gp::launch_return(c->batch, bt->max_pages, pool->num_pages, bt->block_table,
-                               bt->num_pages, pool->free_stack, pool->free_count, action,
-                               c->d_counters, c->d_err, s);
+      return gp::launch_return(w, c->batch, bt->max_pages, pool->num_pages, bt->block_table,
+                               bt->num_pages, pool->free_stack, pool->free_count,
+                               pool->refcount, action, ws, c->d_counters, c->d_err, s);
     });
   return hip_fail(c, e);
 }
@@ -320,7 +327,7 @@ gp_status gp_profile_read(gp_ctx* c, gp_kernel_times* out) {
 
 gp_status gp_get_counters(gp_ctx* c, gp_counters* out) {
   if (!c || !out) return GP_ERR_INVALID_ARG;
-  int64_t h[4];
+  int64_t h[5];
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(h, c->d_counters, sizeof h, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(c, e);
@@ -328,6 +335,7 @@ gp_status gp_get_counters(gp_ctx* c, gp_counters* out) {
   out->compress = h[1];
   out->fallback = h[2];
   out->shrunk = h[3];
+  out->copied = h[4];
   return GP_OK;
 }
 

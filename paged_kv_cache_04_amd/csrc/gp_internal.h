@@ -54,11 +54,17 @@ struct WsHeader {
   int64_t pad[4];
 };
 
+// Per-request state of one gp_compress_hold call (req_flags).
+constexpr int32_t kReqBlocked = 1;    // shared pages could not be replaced: not compressed
+constexpr int32_t kReqCompacted = 2;  // K/V compacted (set by the compaction kernel)
+
 // Workspace: batch plan, calibrated summaries, per-token importance (read by
-// gp_compress_hold), dropped slots, and per-workgroup rings that hold one
-// row's logits and demand distributions at a time.
+// gp_compress_hold), dropped slots, per-request flags and target pages of the
+// prefix-preserving compression, and per-workgroup rings that hold one row's
+// logits and demand distributions at a time.
 struct WsLayout {
-  size_t header, page_off, req_order, qhat, ring_logits, ring_keys, imp, dropped, total;
+  size_t header, page_off, req_order, qhat, ring_logits, ring_keys, imp, dropped, req_flags,
+      target, total;
   int64_t rows, row_tokens, row_pages, ring_tokens, blocks;
 };
 
@@ -82,6 +88,8 @@ inline WsLayout ws_layout(const Params& p, int B, int64_t total_tokens, int64_t 
   w.ring_keys = o;   o = align256(o + sizeof(float) * (size_t)blocks * max_tokens * 2);
   w.imp = o;         o = align256(o + sizeof(float) * (size_t)w.row_tokens);
   w.dropped = o;     o = align256(o + sizeof(int32_t) * (size_t)w.rows * p.b * p.max_freed());
+  w.req_flags = o;   o = align256(o + sizeof(int32_t) * B);
+  w.target = o;      o = align256(o + sizeof(int32_t) * (size_t)(total_tokens / p.b));
   w.total = o;
   return w;
 }
@@ -138,14 +146,15 @@ hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* 
                          const int32_t* k_long, int64_t* k_diff, double* delta,
                          int8_t* decision, hipStream_t s);
 
-hipError_t launch_return(int B, int max_pages, int pool_pages, int32_t* block_table,
-                         int32_t* num_pages, int32_t* free_stack, int32_t* free_count,
-                         const int8_t* action, int64_t* counters, int32_t* err, hipStream_t s);
-
 hipError_t launch_grow(int B, int max_pages, int pool_pages, int32_t* block_table,
                        int32_t* num_pages, const int32_t* free_stack, int32_t* free_count, int reserve,
-                       const int8_t* decision, int8_t* action, int64_t* counters,
-                       int32_t* err, hipStream_t s);
+                       const int8_t* decision, int8_t* action, int32_t* refcount,
+                       int64_t* counters, int32_t* err, hipStream_t s);
+
+hipError_t launch_share(const Params& p, const WsLayout& w, int B, const int8_t* action,
+                        int pool_pages, const int32_t* block_table, int max_pages,
+                        const int32_t* refcount, const int32_t* free_stack, int32_t* free_count,
+                        void* ws, int64_t* counters, int32_t* err, hipStream_t s);
 
 hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t* action,
                          void* ws, int32_t* dropped_out, int32_t* err, hipStream_t s);
@@ -153,6 +162,11 @@ hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t
 hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
                           uint16_t* k_pool, uint16_t* v_pool, int pool_pages,
                           const int32_t* block_table, int max_pages, int32_t* num_tokens,
-                          const void* ws, int64_t* counters, int32_t* err, hipStream_t s);
+                          bool shared, void* ws, int32_t* err, hipStream_t s);
+
+hipError_t launch_return(const WsLayout& w, int B, int max_pages, int pool_pages,
+                         int32_t* block_table, int32_t* num_pages, int32_t* free_stack,
+                         int32_t* free_count, int32_t* refcount, const int8_t* action,
+                         const void* ws, int64_t* counters, int32_t* err, hipStream_t s);
 
 }  // namespace gp

@@ -17,6 +17,11 @@
 // chunk's sources, and every earlier chunk has finished reading, so the
 // in-place move needs no copy of the row.  K and V rows, and different rows,
 // are disjoint and run as separate workgroups.
+// Prefix-preserving compression (App. E.2): a shared page i of the request
+// has a target page, and destinations in page i are written there instead.
+// Sources stay in the old pages, which are only read, so the move is still
+// in place for every other page; rows from the first replaced page on are
+// copied even before the first dropped slot (their destination page is new).
 #include "gp_internal.h"
 
 namespace gp {
@@ -38,12 +43,15 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
                                                  const int32_t* __restrict__ block_table,
                                                  int max_pages, int32_t* __restrict__ num_tokens,
                                                  const int32_t* __restrict__ dropped,
+                                                 const int32_t* __restrict__ target,
+                                                 int32_t* __restrict__ req_flags,
                                                  int32_t* __restrict__ err) {
   __shared__ int32_t gap[2 * kPage];
-  __shared__ int32_t pg[kMaxPages];
+  __shared__ int32_t pg[kMaxPages];   // source pages
+  __shared__ int32_t pgd[kMaxPages];  // destination pages
   __shared__ int64_t s_src[2][kRowsC];
   __shared__ int64_t s_dst[2][kRowsC];
-  __shared__ int bad;
+  __shared__ int bad, first_new;
   if (!hdr->valid) return;
   const int LH = L * Hkv;
   const int row = blockIdx.x >> 1, which = blockIdx.x & 1;
@@ -55,15 +63,28 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
   const int nd = m * b;                    // dropped slots
   const int64_t P = page_off[r + 1] - page_off[r];
   if (P < m + 1) return;
+  if (req_flags[r] & kReqBlocked) return;  // shared pages could not be replaced
   const int l = lh / Hkv, h = lh % Hkv;
   const int t = threadIdx.x;
-  if (t == 0) bad = 0;
+  if (t == 0) {
+    bad = 0;
+    first_new = (int)P;
+  }
   __syncthreads();
   for (int k = t; k < nd; k += kCT) gap[k] = dropped[(int64_t)row * stride + k] - k;
   for (int i = t; i < P; i += kCT) {
     const int page = block_table[(int64_t)r * max_pages + i];
-    if (page < 0 || page >= pool_pages) bad = 1;
+    int dst = page;
+    if (target) {
+      const int tg = target[page_off[r] + i];
+      if (tg >= 0) {
+        dst = tg;
+        atomicMin(&first_new, i);
+      }
+    }
+    if (page < 0 || page >= pool_pages || dst < 0 || dst >= pool_pages) bad = 1;
     pg[i] = page;
+    pgd[i] = dst;
   }
   __syncthreads();
   if (bad) {
@@ -71,15 +92,16 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
     return;
   }
   uint16_t* pool = which ? v_pool : k_pool;
-  // element offset of slot i of this row
-  auto slot_base = [&](int i) -> int64_t {
-    return (((int64_t)l * pool_pages + pg[i >> 8]) * Hkv + h) * (int64_t)(kPage * kD) +
+  // element offset of slot i of this row in physical page `page`
+  auto slot_base = [&](int page, int i) -> int64_t {
+    return (((int64_t)l * pool_pages + page) * Hkv + h) * (int64_t)(kPage * kD) +
            (int64_t)(i & (kPage - 1)) * kD;
   };
   const int end = (int)((P - m) * b);
   const int d0 = gap[0] > 0 ? gap[0] : 0;
+  const int start = first_new * b < d0 ? first_new * b : d0;
   int par = 0;
-  for (int c0 = d0; c0 < end; c0 += kRowsC, par ^= 1) {
+  for (int c0 = start; c0 < end; c0 += kRowsC, par ^= 1) {
     // source and destination offsets of the chunk's destination rows,
     // one binary search per thread (tables alternate between two buffers so
     // the next chunk's tables never overwrite ones still being read)
@@ -91,8 +113,9 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
           const int mid = (lo + hi) >> 1;
           if (gap[mid] <= drow) lo = mid + 1; else hi = mid;
         }
-        s_src[par][t] = slot_base(drow + lo);
-        s_dst[par][t] = slot_base(drow);
+        const int srow = drow + lo;
+        s_src[par][t] = slot_base(pg[srow >> 8], srow);
+        s_dst[par][t] = slot_base(pgd[drow >> 8], drow);
       }
     }
     __syncthreads();
@@ -118,22 +141,26 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
                                     reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8));
     }
   }
-  if (lh == 0 && which == 0 && t == 0) num_tokens[r] = end;
+  if (lh == 0 && which == 0 && t == 0) {
+    num_tokens[r] = end;
+    req_flags[r] = kReqCompacted;
+  }
 }
 
 hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
                           uint16_t* k_pool, uint16_t* v_pool, int pool_pages,
                           const int32_t* block_table, int max_pages, int32_t* num_tokens,
-                          const void* ws, int64_t* counters, int32_t* err, hipStream_t s) {
-  const char* base = static_cast<const char*>(ws);
+                          bool shared, void* ws, int32_t* err, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
   hipLaunchKernelGGL(k_compact, dim3((unsigned)(w.rows * 2)), dim3(kCT), 0, s, p.L, p.Hkv, p.b,
                      p.b * p.max_freed(), pool_pages,
                      reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), action, k_pool, v_pool,
                      block_table, max_pages, num_tokens,
-                     reinterpret_cast<const int32_t*>(base + w.dropped), err);
+                     reinterpret_cast<const int32_t*>(base + w.dropped),
+                     shared ? reinterpret_cast<const int32_t*>(base + w.target) : nullptr,
+                     reinterpret_cast<int32_t*>(base + w.req_flags), err);
   (void)B;
-  (void)counters;
   return hipGetLastError();
 }
 

@@ -77,7 +77,8 @@ hipError_t launch_decide(const Params& p, const WsLayout& w, int B, const void* 
 // rule computed with one block-wide prefix count.  Everyone else, including
 // growing requests that were refused, is marked for compression.
 // A Shrink decision (GrowPage-Shrink policy) passes through as action
-// GP_SHRINK and takes no page.
+// GP_SHRINK and takes no page.  With reference counts (prefix sharing,
+// App. E.2) a granted page gets one reference.
 // counters: [0] pages granted, [1] compress actions, [2] fallbacks.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int pool_pages,
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
                                                     int reserve,
                                                     const int8_t* __restrict__ decision,
                                                     int8_t* __restrict__ action,
+                                                    int32_t* __restrict__ refcount,
                                                     int64_t* __restrict__ counters,
                                                     int32_t* __restrict__ err) {
   __shared__ int scan[kMaxBatch];
@@ -123,6 +125,7 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
       const int page = free_stack[fc - 1 - rank];
       block_table[(int64_t)t * max_pages + P] = page;
       num_pages[t] = P + 1;
+      if (refcount && page >= 0 && page < pool_pages) refcount[page] = 1;
       action[t] = GP_GROW;
     } else if (decision[t] == GP_SHRINK) {
       action[t] = GP_SHRINK;  // needs no page; gp_compress_hold returns one
@@ -144,73 +147,11 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
 
 hipError_t launch_grow(int B, int max_pages, int pool_pages, int32_t* block_table,
                        int32_t* num_pages, const int32_t* free_stack, int32_t* free_count,
-                       int reserve, const int8_t* decision, int8_t* action, int64_t* counters,
-                       int32_t* err, hipStream_t s) {
+                       int reserve, const int8_t* decision, int8_t* action, int32_t* refcount,
+                       int64_t* counters, int32_t* err, hipStream_t s) {
   hipLaunchKernelGGL(k_grow, dim3(1), dim3(kMaxBatch), 0, s, B, max_pages, pool_pages,
                      block_table, num_pages, free_stack, free_count, reserve, decision, action,
-                     counters, err);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Shrink's page return (App. H.1: two pages worth of slots are compacted away
-// and one physical page goes back to the global pool).  Runs after the
-// compaction of the event.  Shrinking requests with at least 3 pages are
-// served in index order (block-wide prefix count): the k-th pushes its last
-// page to free_stack[free_count + k], clears that block-table entry and loses
-// one page.  counters[3] counts the pages returned.  A free count outside
-// [0, pool_pages], or a push beyond the stack, flags GP_DEVERR_PAGES and
-// returns nothing.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kMaxBatch) void k_return(int B, int max_pages, int pool_pages,
-                                                      int32_t* __restrict__ block_table,
-                                                      int32_t* __restrict__ num_pages,
-                                                      int32_t* __restrict__ free_stack,
-                                                      int32_t* __restrict__ free_count,
-                                                      const int8_t* __restrict__ action,
-                                                      int64_t* __restrict__ counters,
-                                                      int32_t* __restrict__ err) {
-  __shared__ int scan[kMaxBatch];
-  const int t = threadIdx.x;
-  const int fc = *free_count;
-  int P = 0;
-  bool want = false;
-  if (t < B && action[t] == GP_SHRINK) {
-    P = num_pages[t];
-    want = P >= 3 && P <= max_pages;
-  }
-  scan[t] = want ? 1 : 0;
-  __syncthreads();
-  for (int off = 1; off < kMaxBatch; off <<= 1) {
-    const int add = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  const int total = scan[kMaxBatch - 1];
-  const bool ok = fc >= 0 && fc + total <= pool_pages;
-  if (!ok) {
-    if (t == 0) atomicOr(err, GP_DEVERR_PAGES);
-    return;
-  }
-  if (want) {
-    const int rank = scan[t] - 1;
-    const int64_t at = (int64_t)t * max_pages + (P - 1);
-    free_stack[fc + rank] = block_table[at];
-    block_table[at] = -1;
-    num_pages[t] = P - 1;
-  }
-  if (t == 0) {
-    *free_count = fc + total;
-    counters[3] += total;
-  }
-}
-
-hipError_t launch_return(int B, int max_pages, int pool_pages, int32_t* block_table,
-                         int32_t* num_pages, int32_t* free_stack, int32_t* free_count,
-                         const int8_t* action, int64_t* counters, int32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(k_return, dim3(1), dim3(kMaxBatch), 0, s, B, max_pages, pool_pages,
-                     block_table, num_pages, free_stack, free_count, action, counters, err);
+                     refcount, counters, err);
   return hipGetLastError();
 }
 

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
                                                  const float* __restrict__ imp,
                                                  int32_t* __restrict__ dropped,
                                                  int32_t* __restrict__ dropped_out,
+                                                 const int32_t* __restrict__ req_flags,
                                                  int32_t* __restrict__ err) {
   __shared__ __attribute__((aligned(16))) float srow[kSelLdsTokens];
   __shared__ uint32_t sloc[kMaxRowTokens / 32];
@@ -282,6 +283,7 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
     if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
     return;
   }
+  if (req_flags[r] & kReqBlocked) return;  // left uncompressed (App. E.2 page shortage)
   const int N = (int)(P * b), nc = N - R;
   const int64_t row_tok = (int64_t)LH * page_off[r] * b + (int64_t)lh * N;
   const float* __restrict__ s = imp + row_tok;
@@ -310,7 +312,8 @@ hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t
                      reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), action,
                      reinterpret_cast<const float*>(base + w.imp),
-                     reinterpret_cast<int32_t*>(base + w.dropped), dropped_out, err);
+                     reinterpret_cast<int32_t*>(base + w.dropped), dropped_out,
+                     reinterpret_cast<const int32_t*>(base + w.req_flags), err);
   (void)B;
   return hipGetLastError();
 }

@@ -33,14 +33,16 @@ def bf16_np(t: torch.Tensor) -> np.ndarray:
 
 
 def runner_for(wl, cfg: gb.Config, want_abar=True, want_dropped=True,
-               qstate: torch.Tensor | None = None) -> BoundaryRunner:
+               qstate: torch.Tensor | None = None,
+               refcount: torch.Tensor | None = None) -> BoundaryRunner:
     """A runner over the workload's current batch state (page counts read
-    back from the device); qstate is reused when given."""
+    back from the device); qstate is reused when given; refcount (int32 per
+    pool page) turns on prefix-preserving compression."""
     s = wl.shape
     if qstate is None:
         qstate = torch.zeros((s.L, wl.max_slots, 2, s.Hq, s.d), dtype=torch.float32,
                              device=wl.device)
-    pool = gb.Pool(wl.k_pool, wl.v_pool, wl.free_stack, wl.free_count)
+    pool = gb.Pool(wl.k_pool, wl.v_pool, wl.free_stack, wl.free_count, refcount)
     batch = gb.Batch(wl.block_table, wl.num_pages, wl.num_tokens, wl.slot, wl.position,
                      wl.num_pages.cpu().numpy().astype(np.int32).copy())
     return BoundaryRunner(cfg, pool, batch, qstate, wl.rope, want_abar=want_abar,
@@ -102,21 +104,38 @@ def device_rows(pool: torch.Tensor, l: int, h: int, pages) -> np.ndarray:
     return bf16_np(pool[l, idx, h].reshape(-1, pool.shape[-1]))
 
 
-def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
-    """A1-A9 on host copies; returns a dict of every output."""
+def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0, refcount=None,
+                 action=None):
+    """A1-A9 on host copies; returns a dict of every output.  refcount (host
+    int32 per pool page) adds the prefix-preserving steps (target pages
+    before the compaction, release after it); action, when given, replaces
+    the grant step (actions chosen by the caller)."""
     dem = oracle.demand(ocfg, lambda r, l, h, pages: hc.keys(l, h, pages),
                         hc.bt, hc.P, state, qcur, hc.rope, hc.pos, hc.slot, want_abar=True)
     bt = hc.bt.copy()
     P = hc.P.copy()
-    action, fc, counters = oracle.grow(dem["decision"], bt, P, hc.free_stack, hc.free_count,
-                                       reserve)
+    rc = None if refcount is None else np.ascontiguousarray(refcount, np.int32).copy()
+    if action is None:
+        action, fc, counters = oracle.grow(dem["decision"], bt, P, hc.free_stack,
+                                           hc.free_count, reserve, refcount=rc)
+    else:
+        action = np.ascontiguousarray(action, np.int8)
+        fc, counters = hc.free_count, None
     B = len(P)
+    # a Shrink action outside the Shrink policy is ignored by the library
+    eff = action.copy()
+    if ocfg.policy != 1:
+        eff[eff == oracle.SHRINK] = oracle.GROW
+    ok = np.ones(B, np.uint8)
+    copied = 0
+    if rc is not None:
+        target, ok, copied, fc = oracle.share_plan(eff, bt, P, rc, hc.free_stack, fc)
     dropped = {}
     compacted = {}
     freed = np.zeros(B, np.int32)  # pages of slots each request frees
     for r in range(B):
-        m = {oracle.COMPRESS: 1, oracle.SHRINK: 2}.get(int(action[r]), 0)
-        if m == 0 or hc.P[r] < m + 1:
+        m = {oracle.COMPRESS: 1, oracle.SHRINK: 2}.get(int(eff[r]), 0)
+        if m == 0 or hc.P[r] < m + 1 or not ok[r]:
             continue
         freed[r] = m
         pages = hc.bt[r, :hc.P[r]]
@@ -130,11 +149,15 @@ def oracle_event(ocfg: OracleConfig, hc: HostCopy, state, qcur, reserve=0):
                 n = oracle.compact(ks, keep)
                 oracle.compact(vs, keep)
                 compacted[(r, l, h)] = (ks[:n], vs[:n])
+    if rc is not None:
+        oracle.share_release(bt, target, ok, rc)
     stack = hc.free_stack.copy()
-    shrunk, fc = oracle.return_pages(action, bt, P, stack, fc)
+    # only requests that were compressed release a page
+    ret = np.where(ok.astype(bool), eff, oracle.COMPRESS).astype(np.int8)
+    shrunk, fc = oracle.return_pages(ret, bt, P, stack, fc, refcount=rc)
     return dict(dem=dem, action=action, bt=bt, P=P, free_count=fc, counters=counters,
                 dropped=dropped, compacted=compacted, freed=freed, free_stack=stack,
-                shrunk=shrunk)
+                shrunk=shrunk, ok=ok, copied=copied, refcount=rc)
 
 
 def row_offsets(P: np.ndarray, L: int, Hkv: int, b: int):

@@ -42,21 +42,34 @@ def test_ema_bit_exact_random_slots():
     assert gb.gp_get_device_errors(ctx) == 0
 
 
-def check_event(wl, cfg, reserve=0, check_f64=True):
+ERR_NOPAGE = 32
+
+
+def check_event(wl, cfg, reserve=0, check_f64=True, refcount=None, action=None):
+    """One event on the GPU and in the oracle on the same inputs, every output
+    compared.  refcount (device int32 per pool page) turns on the
+    prefix-preserving steps; action (host int8 per request), when given, is
+    passed to gp_compress_hold in place of the grant step's."""
     ocfg = oracle_config(cfg)
     hc = HostCopy(wl)
-    run = runner_for(wl, cfg)
+    rc_host = None if refcount is None else refcount.cpu().numpy().copy()
+    run = runner_for(wl, cfg, refcount=refcount)
     q_gpu = run_stream_gpu(run, wl)
     state_o, q_o = run_stream_oracle(wl, ocfg)
     torch.cuda.synchronize()
     assert np.array_equal(run.qstate.cpu().numpy().view(np.uint32), state_o.view(np.uint32)), \
         "summaries differ"
     run.demand(q_gpu)
-    run.grow(reserve_pages=reserve)
-    run.compress()
+    if action is None:
+        run.grow(reserve_pages=reserve)
+        run.compress()
+    else:
+        run.action.copy_(torch.from_numpy(np.asarray(action, np.int8)))
+        run.compress()
     torch.cuda.synchronize()
-    assert run.device_errors() == 0
-    ref = oracle_event(ocfg, hc, state_o, q_o, reserve)
+    errs = run.device_errors()
+    ref = oracle_event(ocfg, hc, state_o, q_o, reserve, refcount=rc_host, action=action)
+    assert errs == (0 if ref["ok"].all() else ERR_NOPAGE), errs
     dem = ref["dem"]
     o = run.out
     assert np.array_equal(o.k_short.cpu().numpy(), dem["ks"]), (o.k_short.cpu().numpy(), dem["ks"])
@@ -87,18 +100,23 @@ def check_event(wl, cfg, reserve=0, check_f64=True):
                 m = want > 1e-30
                 rel = np.abs(got[m] - want[m]) / want[m]
                 assert rel.max() <= 1e-3, rel.max()
-    # grow
+    # grant, page release, pool
     assert np.array_equal(run.action.cpu().numpy(), ref["action"])
     assert np.array_equal(run.batch.block_table.cpu().numpy(), ref["bt"])
     assert np.array_equal(run.batch.num_pages.cpu().numpy(), ref["P"])
     assert int(wl.free_count.item()) == ref["free_count"]
     c = run.counters()
-    assert [c["grown"], c["compress"], c["fallback"]] == list(ref["counters"])
+    if ref["counters"] is not None:
+        assert [c["grown"], c["compress"], c["fallback"]] == list(ref["counters"])
     assert c["shrunk"] == ref["shrunk"]
-    if cfg.policy == 1:
+    assert c["copied"] == ref["copied"]
+    if cfg.policy == 1 or refcount is not None:
         np.testing.assert_array_equal(wl.free_stack.cpu().numpy()[:ref["free_count"]],
                                       ref["free_stack"][:ref["free_count"]])
-    # compress: dropped slots, compacted bytes, token counts
+    if refcount is not None:
+        np.testing.assert_array_equal(refcount.cpu().numpy(), ref["refcount"])
+    # compress: dropped slots, compacted bytes (in the pages the block table
+    # now names), token counts; untouched requests keep every byte
     dropped = run.dropped.cpu().numpy()
     nt = run.batch.num_tokens.cpu().numpy()
     for r in range(len(hc.P)):
@@ -107,12 +125,13 @@ def check_event(wl, cfg, reserve=0, check_f64=True):
         m = int(ref["freed"][r])
         if m > 0:
             assert nt[r] == N - m * ocfg.b
+            new_pages = ref["bt"][r, :ref["P"][r]]
             for l in range(ocfg.L):
                 for h in range(ocfg.Hkv):
                     assert np.array_equal(dropped[r, l, h, :m * ocfg.b], ref["dropped"][(r, l, h)])
                     kw, vw = ref["compacted"][(r, l, h)]
-                    kg = device_rows(wl.k_pool, l, h, pages)[:N - m * ocfg.b]
-                    vg = device_rows(wl.v_pool, l, h, pages)[:N - m * ocfg.b]
+                    kg = device_rows(wl.k_pool, l, h, new_pages)[:N - m * ocfg.b]
+                    vg = device_rows(wl.v_pool, l, h, new_pages)[:N - m * ocfg.b]
                     assert np.array_equal(kg, kw) and np.array_equal(vg, vw), (r, l, h)
         else:
             assert nt[r] == N
@@ -121,6 +140,15 @@ def check_event(wl, cfg, reserve=0, check_f64=True):
                 for h in range(ocfg.Hkv):
                     assert np.array_equal(device_rows(wl.k_pool, l, h, pages), hc.keys(l, h, pages))
                     assert np.array_equal(device_rows(wl.v_pool, l, h, pages), hc.values(l, h, pages))
+    # a page shared before the event is never written (App. E.2)
+    if rc_host is not None:
+        shared = np.nonzero(rc_host > 1)[0]
+        shared = shared[np.isin(shared, hc.used)]
+        for l in range(ocfg.L):
+            for h in range(ocfg.Hkv):
+                assert np.array_equal(device_rows(wl.k_pool, l, h, shared), hc.keys(l, h, shared))
+                assert np.array_equal(device_rows(wl.v_pool, l, h, shared),
+                                      hc.values(l, h, shared))
     return ref
 
 
