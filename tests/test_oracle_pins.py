@@ -465,6 +465,23 @@ def test_grow_pool_arithmetic_and_fallback():
     assert list(action) == [1, 0, 0, 0, 0, 0] and fc == 2 and list(cnt) == [1, 5, 3]
 
 
+def test_grow_sets_reference_of_granted_page():
+    """With reference counts (Appendix E.2: Grow appends a new page and leaves
+    shared pages alone), each granted page is held once; no other count moves."""
+    decision = np.array([1, 0, 1], np.int8)
+    bt = np.array([[1, 2, -1], [1, 3, -1], [4, -1, -1]], np.int32)
+    P = np.array([2, 2, 1], np.int32)
+    rc = np.zeros(12, np.int32)
+    rc[1], rc[2], rc[3], rc[4] = 2, 1, 1, 1
+    before = rc.copy()
+    stack = np.array([10, 11], np.int32)
+    action, fc, _ = oracle.grow(decision, bt, P, stack, 2, refcount=rc)
+    assert list(action) == [1, 0, 1] and bt[0, 2] == 11 and bt[2, 1] == 10
+    assert rc[11] == 1 and rc[10] == 1
+    changed = np.nonzero(rc != before)[0]
+    assert sorted(changed) == [10, 11]
+
+
 # ---------------------------------------------------------------- select --
 
 def _check_selection(s, keep, N, b, R, k_loc, pages=1):
