@@ -388,3 +388,50 @@ def row_f64(keys_f64: np.ndarray, qh_f64: np.ndarray, b: int, p: float = 0.99):
     a_dem = softmax_f64(lg[..., :ndem]).mean(axis=1) if ndem > 0 else np.zeros((2, 0))
     dps = [dp_f64(a_dem[x], p) if ndem > 0 else 0 for x in range(2)]
     return dict(abar_all=a_all.T.copy(), abar_dem=a_dem.T.copy(), dp=np.array(dps), logits=lg)
+
+
+# ---------------------------------------------------------------------------
+# Decode step (fp64 definition mode): the regular decoding path whose
+# attention kernel also carries the summary update (§4.1 "Lightweight
+# Per-Request State Management"; App. E.1 "Initialization and online
+# update"), and the retained-subset output of §3.1 Eq. 3 and Eq. 5.
+# ---------------------------------------------------------------------------
+
+def rope_f64(x: np.ndarray, rope_row: np.ndarray) -> np.ndarray:
+    """Rotary embedding at one position, pairs (j, j + d/2): the same
+    rotate-half convention the cached keys were stored with.  x [..][d]."""
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    c = rope_row[:h].astype(np.float64)
+    s = rope_row[h:].astype(np.float64)
+    return np.concatenate([x[..., :h] * c - x[..., h:] * s, x[..., h:] * c + x[..., :h] * s],
+                          axis=-1)
+
+
+def decode_attention_f64(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                         rope_row: np.ndarray):
+    """Full-cache attention output o_t of §3.1 Eq. 3 for the G query heads
+    of one KV head at one decode step.  q [G][d] (normalised, pre-RoPE),
+    keys / values [N][d] bf16 bits (keys post-RoPE at their own positions).
+    The query is rotated to its position and scaled by 1/sqrt(d); each head
+    takes a softmax over the N slots.  Returns (o [G][d], a [G][N])."""
+    d = q.shape[-1]
+    qh = rope_f64(q, rope_row) / np.sqrt(d)
+    a = softmax_f64(qh @ bf16_to_f64(keys).T)
+    return a @ bf16_to_f64(values), a
+
+
+def subset_output_f64(a: np.ndarray, values: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """Retained-subset output of §3.1 Eq. 3: weights a on the slots of keep,
+    renormalised by their mass m(S).  a [G][N], values [N][d] bf16 bits,
+    keep [N] bool."""
+    keep = np.asarray(keep, dtype=bool)
+    m = a[:, keep].sum(axis=1, keepdims=True)
+    return (a[:, keep] / m) @ bf16_to_f64(values)[keep]
+
+
+def worst_case_error_f64(a: np.ndarray, keep: np.ndarray, v_max: float) -> np.ndarray:
+    """§3.1 Eq. 5: sup over values of norm at most v_max of the output error
+    of retaining keep, = 2 v_max (1 - m(S)), per head.  a [G][N]."""
+    keep = np.asarray(keep, dtype=bool)
+    return 2.0 * v_max * (1.0 - a[:, keep].sum(axis=1))
