@@ -239,6 +239,45 @@ gp_status gp_compress_hold(gp_ctx* ctx, const gp_pool* pool, const gp_batch* bat
                            size_t workspace_bytes, int32_t* dropped_out,
                            void* stream);
 
+/* Workspace bytes gp_decode_attention needs for `batch` requests holding
+ * `total_pages` pages in all (sum of num_pages_host).  Returns 0 on invalid
+ * arguments. */
+size_t gp_decode_workspace_bytes(const gp_ctx* ctx, int32_t batch, int64_t total_pages);
+
+/* Decode-step attention of one layer with the summary update fused (§4.1:
+ * the regular decoding path's attention kernel also updates both summaries
+ * from the normalised pre-RoPE query; App. E.1 "Initialization and online
+ * update"; the output is §3.1 Eq. 3's full-cache o_t).  For each request r
+ * and query head g of the layer `layer`:
+ *   qhat = RoPE(q[r][g], position[r]) / sqrt(d)   (rotate-half pairs j, j+d/2)
+ *   a_i  = softmax over the num_tokens[r] cached slots i of qhat . k_i, where
+ *          logical slot i lives in page block_table[r][i / b] at offset i % b
+ *          and query head g reads KV head g / (Hq / Hkv)
+ *   out[r][g] = sum_i a_i v_i.
+ * Any 1 <= num_tokens[r] <= num_pages[r] * b is allowed (mid-page decoding;
+ * after Compress & Hold num_tokens = (P-1) b covers the compacted slots).
+ * If qstate != NULL the layer's two summaries of slot[r] are updated from q
+ * exactly as gp_update_summaries does (first_step may be NULL: no request is
+ * on its first step), so calling this for every layer equals one
+ * gp_update_summaries call bit for bit.
+ *   q:     device fp32 [B][Hq][d], normalised, before RoPE (read only)
+ *   out:   device fp32 [B][Hq][d] (written)
+ *   rope:  device fp32 [rope_rows][d] (cos of the d/2 frequencies, then sin)
+ *   workspace: gp_decode_workspace_bytes(ctx, B, sum of num_pages_host) bytes
+ * Arithmetic is fp32 (hardware exp2): within 1e-3 of the largest |v| of the
+ * row element-wise against the fp64 definition.  Device checks: counts
+ * outside 1 <= N <= P b or P outside [1, max_pages] set GP_DEVERR_PAGES and
+ * give a zero output (so does a device page total above the host mirror's,
+ * which the workspace was sized for); a page id outside the pool sets
+ * GP_DEVERR_PAGE and its slots are skipped; position and slot as in gp_demand and
+ * gp_update_summaries.  Enqueued on `stream`; pool, batch, q, qstate, rope,
+ * out and workspace are borrowed for the call. */
+gp_status gp_decode_attention(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
+                              int32_t layer, const float* q, float* qstate,
+                              const uint8_t* first_step, const float* rope, int32_t rope_rows,
+                              float* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Kernels of the event, for gp_profile_read. */
 enum gp_kernel_id {
   GP_K_EMA = 0,     /* A0 summary update */
@@ -252,7 +291,8 @@ enum gp_kernel_id {
   GP_K_RETURN = 8,  /* page bookkeeping after compaction: shared-page release, Shrink's
                        page return (prefix sharing or GP_POLICY_SHRINK only) */
   GP_K_SHARE = 9,   /* target pages for shared pages (prefix sharing only) */
-  GP_NUM_KERNELS = 10
+  GP_K_DECODE = 10, /* decode-step attention with the summary update (both kernels) */
+  GP_NUM_KERNELS = 11
 };
 
 typedef struct gp_kernel_times {

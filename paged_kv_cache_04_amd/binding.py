@@ -26,10 +26,11 @@ SYMBOLS = (
     "gp_create", "gp_destroy", "gp_workspace_bytes", "gp_update_summaries", "gp_demand",
     "gp_grow_page", "gp_compress_hold", "gp_get_counters", "gp_get_device_errors",
     "gp_status_str", "gp_last_hip_error", "gp_profile", "gp_profile_read",
+    "gp_decode_workspace_bytes", "gp_decode_attention",
 )
 
 KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact", "return",
-           "share")
+           "share", "decode")
 
 
 class GPError(RuntimeError):
@@ -112,6 +113,11 @@ def load(path: str = LIB_PATH):
     L.gp_compress_hold.argtypes = [vp, ctypes.POINTER(gp_pool), ctypes.POINTER(gp_batch), vp,
                                    vp, sz, vp, vp]
     L.gp_compress_hold.restype = ctypes.c_int
+    L.gp_decode_workspace_bytes.argtypes = [vp, i32, i64]
+    L.gp_decode_workspace_bytes.restype = sz
+    L.gp_decode_attention.argtypes = [vp, ctypes.POINTER(gp_pool), ctypes.POINTER(gp_batch), i32,
+                                      vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    L.gp_decode_attention.restype = ctypes.c_int
     L.gp_get_counters.argtypes = [vp, ctypes.POINTER(gp_counters)]
     L.gp_get_counters.restype = ctypes.c_int
     L.gp_get_device_errors.argtypes = [vp, ctypes.POINTER(i32)]
@@ -292,6 +298,20 @@ def gp_compress_hold(ctx: Context, pool: Pool, batch: Batch, action, workspace,
     _check(load().gp_compress_hold(ctx.handle, ctypes.byref(p), ctypes.byref(b), _ptr(action),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _ptr(dropped_out), _stream(stream)), "gp_compress_hold", ctx)
+
+
+def gp_decode_workspace_bytes(ctx: Context, batch: int, total_pages: int) -> int:
+    return int(load().gp_decode_workspace_bytes(ctx.handle, batch, total_pages))
+
+
+def gp_decode_attention(ctx: Context, pool: Pool, batch: Batch, layer: int, q, qstate, first_step,
+                        rope, out, workspace, stream=None):
+    p, b = pool.c(), batch.c()
+    _check(load().gp_decode_attention(ctx.handle, ctypes.byref(p), ctypes.byref(b), int(layer),
+                                      _ptr(q), _ptr(qstate), _ptr(first_step), _ptr(rope),
+                                      int(rope.shape[0]), _ptr(out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "gp_decode_attention", ctx)
 
 
 def gp_get_counters(ctx: Context) -> dict:

@@ -284,6 +284,34 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   return hip_fail(c, e);
 }
 
+size_t gp_decode_workspace_bytes(const gp_ctx* c, int32_t batch, int64_t total_pages) {
+  if (!c || batch < 1 || total_pages < 1) return 0;
+  return gp::decode_ws_layout(c->p, batch, total_pages).total;
+}
+
+gp_status gp_decode_attention(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, int32_t layer,
+                              const float* q, float* qstate, const uint8_t* first_step,
+                              const float* rope, int32_t rope_rows, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!c || !q || !rope || rope_rows < 1 || !out || !ws) return GP_ERR_INVALID_ARG;
+  if (!shape_supported(c->p)) return GP_ERR_UNSUPPORTED;
+  if (layer < 0 || layer >= c->p.L) return GP_ERR_INVALID_ARG;
+  int64_t total_pages = 0, max_pages_used = 0;
+  gp_status st = check_batch(c, pool, bt, &total_pages, &max_pages_used);
+  if (st != GP_OK) return st;
+  const gp::DecodeWs w = gp::decode_ws_layout(c->p, bt->batch, total_pages);
+  if (ws_bytes < w.total) return GP_ERR_WORKSPACE;
+  if (w.unit_cap > INT32_MAX) return GP_ERR_UNSUPPORTED;
+  const int unit_blocks = c->num_cus * GP_DECODE_BLOCKS_PER_CU;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_fail(c, timed(c, GP_K_DECODE, s, [&] {
+    return gp::launch_decode(c->p, w, bt->batch, layer, pool->k_pool, pool->v_pool,
+                             pool->num_pages, bt->block_table, bt->max_pages, bt->num_pages,
+                             bt->num_tokens, bt->slot, bt->position, q, qstate, first_step, rope,
+                             rope_rows, unit_blocks, ws, out, c->d_err, s);
+  }));
+}
+
 gp_status gp_profile(gp_ctx* c, int enable) {
   if (!c) return GP_ERR_INVALID_ARG;
   if (enable) {

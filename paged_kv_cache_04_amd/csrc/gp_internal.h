@@ -25,6 +25,10 @@ constexpr int64_t kMaxRequestTokens = int64_t(1) << 23;
 #define GP_DEMAND_BLOCKS_PER_CU 1
 #endif
 constexpr int kDemandBlocksPerCU = GP_DEMAND_BLOCKS_PER_CU;
+// Decode attention: persistent workgroups per CU of the unit kernel.
+#ifndef GP_DECODE_BLOCKS_PER_CU
+#define GP_DECODE_BLOCKS_PER_CU 2
+#endif
 constexpr uint64_t kWsMagic = 0x4750574b53503031ull;  // "GPWKSP01"
 
 // Fixed-point scale for exact, order-free sums of probabilities: values in
@@ -168,5 +172,22 @@ hipError_t launch_return(const WsLayout& w, int B, int max_pages, int pool_pages
                          int32_t* block_table, int32_t* num_pages, int32_t* free_stack,
                          int32_t* free_count, int32_t* refcount, const int8_t* action,
                          const void* ws, int64_t* counters, int32_t* err, hipStream_t s);
+
+// Decode-attention workspace: rotated queries, unit list, per-request page
+// prefix, unit count, per-unit partials.
+struct DecodeWs {
+  size_t qhat, units, page_pre, n_units, part, total;
+  int64_t unit_cap;
+};
+
+DecodeWs decode_ws_layout(const Params& p, int B, int64_t total_pages);
+
+hipError_t launch_decode(const Params& p, const DecodeWs& w, int B, int layer,
+                         const uint16_t* k_pool, const uint16_t* v_pool, int pool_pages,
+                         const int32_t* block_table, int max_pages, const int32_t* num_pages,
+                         const int32_t* num_tokens, const int32_t* slot, const int32_t* position,
+                         const float* q, float* qstate, const uint8_t* first, const float* rope,
+                         int rope_rows, int unit_blocks, void* ws, float* out, int32_t* err,
+                         hipStream_t s);
 
 }  // namespace gp

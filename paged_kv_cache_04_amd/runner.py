@@ -66,3 +66,32 @@ class BoundaryRunner:
 
     def counters(self) -> dict:
         return gb.gp_get_counters(self.ctx)
+
+
+class DecodeRunner:
+    """Decode-step attention over a batch, one layer per call, through the C
+    ABI; owns the workspace and the output for a fixed batch shape."""
+
+    def __init__(self, cfg: gb.Config, pool: gb.Pool, batch: gb.Batch, rope: torch.Tensor,
+                 ctx: gb.Context | None = None):
+        self.cfg = cfg
+        self.ctx = gb.Context(cfg) if ctx is None else ctx
+        self.pool = pool
+        self.batch = batch
+        self.rope = rope
+        dev = rope.device
+        B = batch.block_table.shape[0]
+        self.ws = torch.empty(gb.gp_decode_workspace_bytes(
+            self.ctx, B, int(batch.num_pages_host.astype(np.int64).sum())),
+            dtype=torch.uint8, device=dev)
+        self.out = torch.empty((B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32,
+                               device=dev)
+
+    def layer(self, layer: int, q: torch.Tensor, qstate: torch.Tensor | None = None,
+              first_step: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        gb.gp_decode_attention(self.ctx, self.pool, self.batch, layer, q, qstate, first_step,
+                               self.rope, self.out, self.ws, stream)
+        return self.out
+
+    def device_errors(self) -> int:
+        return gb.gp_get_device_errors(self.ctx)
