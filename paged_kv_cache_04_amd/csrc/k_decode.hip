@@ -8,31 +8,30 @@
 // Three kernels:
 //  1. prep, a workgroup per request: the summary update, the rotated and
 //     scaled queries of all heads (to the workspace), and the request's work
-//     units, one per (cached page, KV head), at its offset in the batch list;
-//  2. units, persistent: every wave walks the unit list with a stride of all
-//     waves of the grid and computes, for the 4 query heads of the unit's KV
-//     head, the page's maximum logit, its sum of exp(l - max) and the
-//     unnormalised sum of exp(l - max) v.  A wave reads its page's 64 KiB of
-//     K and 64 KiB of V as one sequential stream of 16-byte loads; this
-//     one-stream-per-wave order reads HBM markedly faster than workgroups
-//     whose waves share the pages of one token range;
-//  3. merge, a workgroup per (request, KV head): combines the pages.
-// Work units never straddle requests, so each wave's running sums need no
-// cross-wave synchronisation; the partials cost 2 KiB per page and head.
-// Inside a unit, lanes own slices of the head dimension: 16 lanes hold one
+//     units, one per (KV head, cached page), at its offset in the batch list;
+//  2. units, persistent: the unit list is cut into equal contiguous ranges,
+//     one per wave, so the work is balanced to a page.  For the 4 query
+//     heads of a unit's KV head a wave computes the running maximum logit,
+//     sum of exp(l - max) and unnormalised sum of exp(l - max) v over runs of
+//     pages of one (request, KV head), writing one partial per run.  A wave
+//     reads its pages' 64 KiB of K and 64 KiB of V as one sequential stream
+//     of 16-byte loads: one stream per wave reads HBM markedly faster than
+//     workgroups whose waves share one token range;
+//  3. merge, a workgroup per (request, KV head): combines its runs.
+// Inside a page, lanes own slices of the head dimension: 16 lanes hold one
 // token's 128 elements (8 each, one 16-byte load of K and one of V), so a
 // load instruction reads 4 whole consecutive rows, and the query's slice of
 // all 4 heads (32 values) stays in registers.  Pass 1 streams the page's
-// keys, 32 tokens per step (8 loads per lane, the next step's loads issued as
-// soon as the current ones are consumed), reduces the 32 partial dot products
-// of a step's 8 tokens x 4 heads across the row's 16 lanes by a transposed
-// DPP reduction (each lane ends with 2 complete logits) and stores the
-// logits in the wave's LDS stage; the page maximum is known at its end, so
-// each weight exp(l - max) is taken once, in place, with no rescaling; pass 2
-// streams the values and accumulates them with the weights read from LDS.  The path reads K
-// and V once: 512 bytes per cached token and KV head, HBM-bound.  Arithmetic
-// is fp32 with the hardware exp2; results are compared with the fp64
-// definition within a stated tolerance.
+// keys, 32 tokens per step (8 loads per lane; two register buffers hold
+// alternate steps, so the next step's loads are always in flight), reduces
+// the 32 partial dot products of a step's 8 tokens x 4 heads across the
+// row's 16 lanes by a transposed DPP reduction (each lane ends with 2
+// complete logits) and stores the logits in the wave's LDS stage; with the
+// page maximum known, each weight exp(l - max) is taken once, in place;
+// pass 2 streams the values and accumulates them with the weights read from
+// LDS.  The path reads K and V once: 512 bytes per cached token and KV head,
+// HBM-bound.  Arithmetic is fp32 with the hardware exp2; results are
+// compared with the fp64 definition within a stated tolerance.
 #include "gp_internal.h"
 
 namespace gp {
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(kDecT) void k_decode_prep(DecodeArgs a) {
   }
   // pages of the requests before this one and of the whole batch (0 for a
   // request with inconsistent counts), then this request's units, in
-  // (request, page, KV head) order
+  // (request, KV head, page) order
   __shared__ int red[2][kDecWaves];
   int before = 0, all = 0;
   for (int i = t; i < a.B; i += kDecT) {
@@ -169,63 +168,191 @@ __global__ __launch_bounds__(kDecT) void k_decode_prep(DecodeArgs a) {
   const int own = N < 0 ? 0 : (N + kPage - 1) / kPage;
   if (fits)
     for (int k = t; k < own * a.Hkv; k += kDecT)
-      a.units[(int64_t)before * a.Hkv + k] = make_int2(r * a.Hkv + k % a.Hkv, k / a.Hkv);
+      a.units[(int64_t)before * a.Hkv + k] = make_int2(r * a.Hkv + k / own, k % own);
 }
 
 // ---- 2. units -----------------------------------------------------------------
-// Per unit, two passes over the page: the keys (logits to the wave's LDS
-// stage, the page maximum per head), then the weights exp(l - max) in place
-// with their sums, then the values.  The wave's memory stream is the K tile
-// followed by the V tile, and no running sum is ever rescaled.
+// The unit list is cut into equal contiguous ranges, one per wave.  Units are
+// in (request, KV head, page) order, so a wave's range is a few runs of
+// consecutive pages of one (request, KV head); the wave keeps running sums
+// over a run and writes one partial per run, at the run's first unit index
+// (a partial per page would add writes between the reads, which costs HBM
+// time far beyond their size).  Per page, two passes: the keys (logits to
+// the wave's LDS stage, the page maximum per head; the running maximum grows
+// and the running sums are rescaled once if it does), then the weights
+// exp(l - max) in place, then the values.  The wave's loads form one stream
+// over its range: each page contributes its key steps, then its value steps
+// (each part padded to an even number of steps), and two register buffers
+// take alternate steps, refilled with the step two ahead as soon as they are
+// consumed, so the next step's loads, also the first ones of the next page,
+// are always in flight.
+struct UnitRef {
+  const uint16_t* kp;
+  const uint16_t* vp;
+  int rh, r, h, n_tok, ns, nsk, len;  // tokens, 32-token steps, first value step, stream length
+  bool ok, valid;
+};
+
+__device__ __forceinline__ UnitRef unit_ref(const DecodeArgs& a, int u, int u_end) {
+  UnitRef x{};
+  x.valid = u < u_end;
+  if (!x.valid) return x;
+  const int2 e = a.units[u];
+  x.rh = __builtin_amdgcn_readfirstlane(e.x);
+  const int pg = __builtin_amdgcn_readfirstlane(e.y);
+  x.r = x.rh / a.Hkv;
+  x.h = x.rh % a.Hkv;
+  const int begin = pg * kPage;
+  x.n_tok = min(__builtin_amdgcn_readfirstlane(a.num_tokens[x.r]), begin + kPage) - begin;
+  x.ns = (x.n_tok + kStep - 1) / kStep;
+  x.nsk = x.ns + (x.ns & 1);
+  x.len = 2 * x.nsk;
+  const int page =
+      __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)x.r * a.max_pages + pg]);
+  x.ok = page >= 0 && page < a.pool_pages;
+  const int64_t base =
+      (((int64_t)a.layer * a.pool_pages + (x.ok ? page : 0)) * a.Hkv + x.h) * (int64_t)kPage * kD;
+  x.kp = a.k_pool + base;
+  x.vp = a.v_pool + base;
+  return x;
+}
+
+// units per wave range
+__device__ __forceinline__ int unit_range(int n_units, int waves) {
+  return (n_units + waves - 1) / waves;
+}
+
 __global__ __launch_bounds__(kDecT) void k_decode_units(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float lgs[kDecWaves][kPage][kGroup];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = __builtin_amdgcn_readfirstlane(*a.n_units);
+  const int R = unit_range(n_units, gridDim.x * kDecWaves);
+  const int u_begin = (blockIdx.x * kDecWaves + w) * R;
+  const int u_end = min(u_begin + R, n_units);
+  if (u_begin >= u_end) return;
   const int sub = lane & 15, grp = lane >> 4;  // slice of d, token within a group of 4
   // lane bits within its row of 16, used by the transposed reduction
   const bool b3 = sub & 8, b2 = sub & 4, b1 = sub & 2, b0 = sub & 1;
   const int my_i = sub >> 1;  // token group whose logits of heads 2 b0, 2 b0 + 1 this lane ends with
+  const int hl = lane & 3;    // head of this lane's weight entries
   float(*lw)[kGroup] = lgs[w];
-  const int64_t head_stride = (int64_t)kPage * kD;  // elements per (page, KV head)
-  for (int u = blockIdx.x * kDecWaves + w; u < n_units; u += gridDim.x * kDecWaves) {
-    const int2 e = a.units[u];
-    const int rh = __builtin_amdgcn_readfirstlane(e.x), pg = __builtin_amdgcn_readfirstlane(e.y);
-    const int r = rh / a.Hkv, h = rh % a.Hkv;
-    const int begin = pg * kPage;
-    const int end = min(__builtin_amdgcn_readfirstlane(a.num_tokens[r]), begin + kPage);
-    const int n_tok = end - begin;                           // 1 .. 256
-    const int n_pad = (n_tok + kStep - 1) / kStep * kStep;  // slots the steps cover
-    const int page = a.block_table[(int64_t)r * a.max_pages + pg];
-    const bool ok = page >= 0 && page < a.pool_pages;
-    if (!ok && lane == 0) atomicOr(a.err, GP_DEVERR_PAGE);
-    const int64_t base =
-        (((int64_t)a.layer * a.pool_pages + (ok ? page : 0)) * a.Hkv + h) * head_stride;
-    const uint16_t* kp = a.k_pool + base;
-    const uint16_t* vp = a.v_pool + base;
-    // element offset of token group i of the step at slot c (clamped to the
-    // step's first slot past the end, so every load stays inside the tile)
-    auto row_off = [&](int c, int i) -> int64_t {
-      const int tok = c + 4 * i + grp;
-      return (int64_t)(tok < n_tok ? tok : c) * kD + sub * 8;
-    };
-    u32x4 kv[8];
+  // step si of unit x's stream into buf (nothing for a pad or past the end);
+  // element offsets of token group i of a step at slot c are clamped to the
+  // step's first slot past the unit's end, so every load stays in the tile
+  auto issue_x = [&](const UnitRef& x, int si, u32x4 (&buf)[8]) {
+    if (!x.valid) return;
+    const uint16_t* src;
+    int c;
+    if (si < x.ns) {
+      src = x.kp;
+      c = si * kStep;
+    } else if (si >= x.nsk && si < x.nsk + x.ns) {
+      src = x.vp;
+      c = (si - x.nsk) * kStep;
+    } else {
+      return;
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + row_off(0, i)));
-    // the query slices of the 4 heads
-    float qs[kGroup][8];
+    for (int i = 0; i < 8; ++i) {
+      const int tok = c + 4 * i + grp;
+      const uint32_t off = (uint32_t)((tok < x.n_tok ? tok : c) * kD + sub * 8);  // < 2^15
+      buf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
+    }
+  };
+  // the query slices of the 4 heads of unit x (loaded one unit ahead: the
+  // load counter is in order, so loads issued after the stream would make
+  // their first use wait for the whole stream)
+  auto load_q = [&](const UnitRef& x, float (&q)[kGroup][8]) {
+    if (!x.valid) return;
 #pragma unroll
     for (int gg = 0; gg < kGroup; ++gg) {
       const float4* qp = reinterpret_cast<const float4*>(
-          a.qhat + ((int64_t)r * a.Hq + h * kGroup + gg) * kD + sub * 8);
-      const float4 x = qp[0], y = qp[1];
-      qs[gg][0] = x.x; qs[gg][1] = x.y; qs[gg][2] = x.z; qs[gg][3] = x.w;
-      qs[gg][4] = y.x; qs[gg][5] = y.y; qs[gg][6] = y.z; qs[gg][7] = y.w;
+          a.qhat + ((int64_t)x.r * a.Hq + x.h * kGroup + gg) * kD + sub * 8);
+      const float4 x0 = qp[0], y0 = qp[1];
+      q[gg][0] = x0.x; q[gg][1] = x0.y; q[gg][2] = x0.z; q[gg][3] = x0.w;
+      q[gg][4] = y0.x; q[gg][5] = y0.y; q[gg][6] = y0.z; q[gg][7] = y0.w;
     }
-    // -- pass 1: logits ---------------------------------------------------------
+  };
+  // running state of the current run: maxima per head (all lanes), weight
+  // sum of head hl (per lane), value sums (per lane, over its token rows)
+  float M[kGroup], s_l, acc[kGroup][8];
+  auto reset = [&]() {
+#pragma unroll
+    for (int gg = 0; gg < kGroup; ++gg) {
+      M[gg] = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[gg][k] = 0.0f;
+    }
+    s_l = 0.0f;
+  };
+  auto flush = [&](int u_first) {
+    // sum over the lanes of one head (same lane & 3): row_ror 4 and 8, then rows
+    float st = s_l;
+    st += dpp_f<0x124>(st);
+    st += dpp_f<0x128>(st);
+    st += __shfl_xor(st, 16);
+    st += __shfl_xor(st, 32);
+    // merge the wave's 4 token rows (lanes l, l^16, l^32, l^48)
+#pragma unroll
+    for (int gg = 0; gg < kGroup; ++gg) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc[gg][k] += __shfl_xor(acc[gg][k], 16);
+        acc[gg][k] += __shfl_xor(acc[gg][k], 32);
+      }
+    }
+    float* pp = a.part + (int64_t)u_first * kPartStride;
+    if (lane < 16) {
+#pragma unroll
+      for (int gg = 0; gg < kGroup; ++gg) {
+        float4* o = reinterpret_cast<float4*>(pp + gg * kD + sub * 8);
+        o[0] = make_float4(acc[gg][0], acc[gg][1], acc[gg][2], acc[gg][3]);
+        o[1] = make_float4(acc[gg][4], acc[gg][5], acc[gg][6], acc[gg][7]);
+      }
+    }
+    if (lane < kGroup) {
+      pp[kGroup * kD + lane] = lane == 0 ? M[0] : lane == 1 ? M[1] : lane == 2 ? M[2] : M[3];
+      pp[kGroup * kD + kGroup + lane] = st;
+    }
+  };
+
+  int u = u_begin;
+  UnitRef cur = unit_ref(a, u, u_end);
+  float qs_next[kGroup][8];
+  load_q(cur, qs_next);
+  u32x4 bufA[8], bufB[8];
+  issue_x(cur, 0, bufA);
+  issue_x(cur, 1, bufB);
+  int run_first = u, run_rh = cur.rh;
+  reset();
+  while (cur.valid) {
+    const UnitRef nxt = unit_ref(a, u + 1, u_end);
+    auto issue = [&](int si, u32x4 (&buf)[8]) {
+      if (si < cur.len) issue_x(cur, si, buf);
+      else issue_x(nxt, si - cur.len, buf);
+    };
+    if (cur.rh != run_rh) {  // a new (request, KV head): close the run
+      flush(run_first);
+      reset();
+      run_first = u;
+      run_rh = cur.rh;
+    }
+    const int n_tok = cur.n_tok, ns = cur.ns, nsk = cur.nsk;
+    const bool ok = cur.ok;
+    const int n_pad = ns * kStep;  // slots the steps cover
+    if (!ok && lane == 0) atomicOr(a.err, GP_DEVERR_PAGE);
+    float qs[kGroup][8];
+#pragma unroll
+    for (int gg = 0; gg < kGroup; ++gg)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qs[gg][k] = qs_next[gg][k];
+    if (nxt.valid && nxt.rh != cur.rh) load_q(nxt, qs_next);
     float mx0 = -INFINITY, mx1 = -INFINITY;  // this lane's heads 2 b0, 2 b0 + 1
-    for (int c0 = 0; c0 < n_tok; c0 += kStep) {
+
+    // pass 1 step: logits of 32 tokens
+    auto key_step = [&](int si, u32x4 (&kv)[8]) {
+      const int c0 = si * kStep;
       // partial dot products over this lane's 8 elements: v[i * 4 + g]
       float v[8 * kGroup];
 #pragma unroll
@@ -246,18 +373,7 @@ __global__ __launch_bounds__(kDecT) void k_decode_units(DecodeArgs a) {
           v[i * kGroup + gg] = d;
         }
       }
-      // the next step's keys (or the first values) go into the registers just
-      // consumed
-      const int cn = c0 + kStep;
-      if (cn < n_tok) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + row_off(cn, i)));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + row_off(0, i)));
-      }
+      issue(si + 2, kv);
       // transposed reduction over the 16 lanes of the row: at each step a
       // lane keeps the half of its values selected by one lane bit and adds
       // the partner's copy of that half (partners sub^8, sub^7, sub^2, sub^1
@@ -290,64 +406,61 @@ __global__ __launch_bounds__(kDecT) void k_decode_units(DecodeArgs a) {
       mx0 = fmaxf(mx0, l0);
       mx1 = fmaxf(mx1, l1);
       *reinterpret_cast<float2*>(&lw[tl][b0 ? 2 : 0]) = make_float2(l0, l1);
-    }
-    // page maximum per head: lanes with the same bit 0 hold the same heads
-    float mh[kGroup];
-    {
-      float y[2] = {mx0, mx1};
+      if (si != ns - 1) return;
+      // end of pass 1: page maximum per head (lanes with the same bit 0 hold
+      // the same heads) raises the running maximum; the running sums are
+      // rescaled when it grows; then the weights exp(l - max) in place,
+      // entry idx = 4 token + head, a lane's entries all of head hl
+      float mh[kGroup];
+      {
+        float y[2] = {mx0, mx1};
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        y[q] = fmaxf(y[q], dpp_f<0x4E>(y[q]));
-        y[q] = fmaxf(y[q], dpp_f<0x124>(y[q]));  // row_ror:4
-        y[q] = fmaxf(y[q], dpp_f<0x128>(y[q]));  // row_ror:8
-        y[q] = fmaxf(y[q], __shfl_xor(y[q], 16));
-        y[q] = fmaxf(y[q], __shfl_xor(y[q], 32));
+        for (int q = 0; q < 2; ++q) {
+          y[q] = fmaxf(y[q], dpp_f<0x4E>(y[q]));
+          y[q] = fmaxf(y[q], dpp_f<0x124>(y[q]));  // row_ror:4
+          y[q] = fmaxf(y[q], dpp_f<0x128>(y[q]));  // row_ror:8
+          y[q] = fmaxf(y[q], __shfl_xor(y[q], 16));
+          y[q] = fmaxf(y[q], __shfl_xor(y[q], 32));
+        }
+        const float o0 = dpp_f<0xB1>(y[0]), o1 = dpp_f<0xB1>(y[1]);  // the other two heads
+        mh[0] = b0 ? o0 : y[0];
+        mh[1] = b0 ? o1 : y[1];
+        mh[2] = b0 ? y[0] : o0;
+        mh[3] = b0 ? y[1] : o1;
       }
-      const float o0 = dpp_f<0xB1>(y[0]), o1 = dpp_f<0xB1>(y[1]);  // the other two heads
-      mh[0] = b0 ? o0 : y[0];
-      mh[1] = b0 ? o1 : y[1];
-      mh[2] = b0 ? y[0] : o0;
-      mh[3] = b0 ? y[1] : o1;
-    }
-    wave_sync();
-    // -- weights in place: entry idx = 4 token + head; a lane's entries all
-    // have head lane & 3 -------------------------------------------------------
-    const int hl = lane & 3;
-    const float m_l = hl == 0 ? mh[0] : hl == 1 ? mh[1] : hl == 2 ? mh[2] : mh[3];
-    float s_l = 0.0f;
-    float* flat = &lw[0][0];
-    for (int idx = lane; idx < n_pad * kGroup; idx += 64) {
-      const float l = flat[idx];
-      const float pv = l == -INFINITY ? 0.0f : exp_fast(l - m_l);
-      flat[idx] = pv;
-      s_l += pv;
-    }
-    // sum over the lanes of one head (same lane & 3): row_ror 4 and 8, then rows
-    s_l += dpp_f<0x124>(s_l);
-    s_l += dpp_f<0x128>(s_l);
-    s_l += __shfl_xor(s_l, 16);
-    s_l += __shfl_xor(s_l, 32);
-    wave_sync();
-    // -- pass 2: values ----------------------------------------------------------
-    float acc[kGroup][8];
+      bool grows = false;
 #pragma unroll
-    for (int gg = 0; gg < kGroup; ++gg)
+      for (int gg = 0; gg < kGroup; ++gg) grows |= mh[gg] > M[gg];
+      if (grows) {  // wave-uniform
+        float f[kGroup];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[gg][k] = 0.0f;
-    for (int c0 = 0; c0 < n_tok; c0 += kStep) {
+        for (int gg = 0; gg < kGroup; ++gg) {
+          const float m_new = fmaxf(M[gg], mh[gg]);
+          f[gg] = exp_fast(M[gg] - m_new);  // 0 while M is -inf
+          M[gg] = m_new;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[gg][k] *= f[gg];
+        }
+        s_l *= hl == 0 ? f[0] : hl == 1 ? f[1] : hl == 2 ? f[2] : f[3];
+      }
+      wave_sync();
+      const float m_l = hl == 0 ? M[0] : hl == 1 ? M[1] : hl == 2 ? M[2] : M[3];
+      float* flat = &lw[0][0];
+      for (int idx = lane; idx < n_pad * kGroup; idx += 64) {
+        const float l = flat[idx];
+        const float pv = l == -INFINITY ? 0.0f : exp_fast(l - m_l);
+        flat[idx] = pv;
+        s_l += pv;
+      }
+      wave_sync();
+    };
+    // pass 2 step: values of 32 tokens times their weights
+    auto value_step = [&](int si, u32x4 (&vv)[8]) {
+      const int c0 = (si - nsk) * kStep;
       float4 pr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         pr[i] = *reinterpret_cast<const float4*>(&lw[c0 + 4 * i + grp][0]);
-      u32x4 vv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vv[i] = kv[i];
-      const int cn = c0 + kStep;
-      if (cn < n_tok) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + row_off(cn, i)));
-      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float vf[8] = {bf16_lo(vv[i].x), bf16_hi(vv[i].x), bf16_lo(vv[i].y),
@@ -359,90 +472,73 @@ __global__ __launch_bounds__(kDecT) void k_decode_units(DecodeArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) acc[gg][k] = __builtin_fmaf(pg4[gg], vf[k], acc[gg][k]);
       }
+      issue(si + 2, vv);
+    };
+    for (int si = 0; si < ns; si += 2) {
+      key_step(si, bufA);
+      if (si + 1 < ns) key_step(si + 1, bufB);
+      else issue(si + 3, bufB);  // pad: buffer B takes the second value step
+    }
+    for (int si = nsk; si < cur.len; si += 2) {
+      value_step(si, bufA);
+      if (si + 1 < nsk + ns) value_step(si + 1, bufB);
+      else issue(si + 3, bufB);  // pad: buffer B takes the next unit's second step
     }
     wave_sync();
-    // merge the wave's 4 token rows (lanes l, l^16, l^32, l^48)
-#pragma unroll
-    for (int gg = 0; gg < kGroup; ++gg) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[gg][k] += __shfl_xor(acc[gg][k], 16);
-        acc[gg][k] += __shfl_xor(acc[gg][k], 32);
-      }
-    }
-    float* pp = a.part + (int64_t)u * kPartStride;
-    if (lane < 16) {
-#pragma unroll
-      for (int gg = 0; gg < kGroup; ++gg) {
-        float4* o = reinterpret_cast<float4*>(pp + gg * kD + sub * 8);
-        o[0] = make_float4(acc[gg][0], acc[gg][1], acc[gg][2], acc[gg][3]);
-        o[1] = make_float4(acc[gg][4], acc[gg][5], acc[gg][6], acc[gg][7]);
-      }
-    }
-    if (lane < kGroup) {
-      pp[kGroup * kD + lane] = m_l;
-      pp[kGroup * kD + kGroup + lane] = s_l;
-    }
+    cur = nxt;
+    ++u;
   }
+  flush(run_first);
 }
 
 // ---- 3. merge -------------------------------------------------------------------
-// o = sum_p e^(m_p - m) o_p / sum_p e^(m_p - m) S_p over the request's pages,
-// m the largest page maximum.  1024 threads: the maxima over all threads,
-// then 4 groups of pages summed side by side and added in LDS.
-constexpr int kMergeT = 1024;
+// o = sum_q e^(m_q - m) o_q / sum_q e^(m_q - m) S_q over the partials q of a
+// (request, KV head), m the largest partial maximum.  The request's units
+// are [U0, U0 + np); its partials sit at U0 and at every wave-range start
+// inside it.
+constexpr int kMergeT = 256;
 
-__global__ __launch_bounds__(kMergeT) void k_decode_merge(DecodeArgs a) {
-  __shared__ float s_m[kMergeT / 64][kGroup];
-  __shared__ float s_o[4][kGroup][kD];
-  __shared__ float s_s[4][kGroup];
+__global__ __launch_bounds__(kMergeT) void k_decode_merge(DecodeArgs a, int waves) {
+  __shared__ int s_idx[kMergeT];
   const int t = threadIdx.x;
   const int rh = blockIdx.x;
   const int r = rh / a.Hkv, h = rh % a.Hkv;
+  const int g = t >> 6, j = t & 63;
+  float* orow = a.out + ((int64_t)r * a.Hq + h * kGroup + g) * kD;
   const int N = decode_tokens(a, r);
-  const bool empty = N < 0 || *a.n_units == 0;
-  const int np = empty ? 0 : (N + kPage - 1) / kPage;
-  const float* base = a.part + ((int64_t)a.page_pre[r] * a.Hkv + h) * kPartStride;
-  const int64_t stride = (int64_t)a.Hkv * kPartStride;  // next page, same KV head
-  // maxima: thread t reads head t & 3 of pages t >> 2, (t >> 2) + 256, ...
-  float mloc = -INFINITY;
-  for (int idx = t; idx < np * kGroup; idx += kMergeT)
-    mloc = fmaxf(mloc, base[(idx >> 2) * stride + kGroup * kD + (idx & 3)]);
-#pragma unroll
-  for (int m = 4; m < 64; m <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, m));
-  if ((t & 63) < kGroup) s_m[t >> 6][t & 63] = mloc;
+  const int n_units = *a.n_units;
+  if (N < 0 || n_units == 0) {
+    orow[j] = 0.0f;
+    orow[j + kD / 2] = 0.0f;
+    return;
+  }
+  const int np = (N + kPage - 1) / kPage;
+  const int R = unit_range(n_units, waves);
+  const int U0 = a.page_pre[r] * a.Hkv + h * np, U1 = U0 + np;
+  // partial indices: U0, then the range starts k R in (U0, U1)
+  const int k0 = U0 / R + 1;
+  const int nq = 1 + max(0, (U1 - 1) / R - k0 + 1);
+  for (int q = t; q < nq; q += kMergeT) s_idx[q] = q == 0 ? U0 : (k0 + q - 1) * R;
   __syncthreads();
-  const int grp = t >> 8, g = (t >> 6) & 3, j = t & 63;
+  const int nq_lds = min(nq, kMergeT);
   float m = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kMergeT / 64; ++w) m = fmaxf(m, s_m[w][g]);
+  for (int q = 0; q < nq; ++q) {
+    const int ui = q < nq_lds ? s_idx[q] : (k0 + q - 1) * R;
+    m = fmaxf(m, a.part[(int64_t)ui * kPartStride + kGroup * kD + g]);
+  }
   float o1 = 0.0f, o2 = 0.0f, ssum = 0.0f;
-#pragma unroll 4
-  for (int p = grp; p < np; p += 4) {
-    const float* ps = base + p * stride;
-    const float mp = ps[kGroup * kD + g];
-    const float f = mp == -INFINITY ? 0.0f : exp_fast(mp - m);
+  for (int q = 0; q < nq; ++q) {
+    const int ui = q < nq_lds ? s_idx[q] : (k0 + q - 1) * R;
+    const float* ps = a.part + (int64_t)ui * kPartStride;
+    const float mq = ps[kGroup * kD + g];
+    const float f = mq == -INFINITY ? 0.0f : exp_fast(mq - m);
     o1 = __builtin_fmaf(f, ps[g * kD + j], o1);
     o2 = __builtin_fmaf(f, ps[g * kD + j + kD / 2], o2);
     ssum = __builtin_fmaf(f, ps[kGroup * kD + kGroup + g], ssum);
   }
-  s_o[grp][g][j] = o1;
-  s_o[grp][g][j + kD / 2] = o2;
-  if (j == 0) s_s[grp][g] = ssum;
-  __syncthreads();
-  if (grp == 0) {
-    float x1 = 0.0f, x2 = 0.0f, sv = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      x1 += s_o[q][g][j];
-      x2 += s_o[q][g][j + kD / 2];
-      sv += s_s[q][g];
-    }
-    const float inv = sv > 0.0f ? 1.0f / sv : 0.0f;
-    float* orow = a.out + ((int64_t)r * a.Hq + h * kGroup + g) * kD;
-    orow[j] = x1 * inv;
-    orow[j + kD / 2] = x2 * inv;
-  }
+  const float inv = ssum > 0.0f ? 1.0f / ssum : 0.0f;
+  orow[j] = o1 * inv;
+  orow[j + kD / 2] = o2 * inv;
 }
 
 DecodeWs decode_ws_layout(const Params& p, int B, int64_t total_pages) {
@@ -503,7 +599,8 @@ hipError_t launch_decode(const Params& p, const DecodeWs& w, int B, int layer,
   hipLaunchKernelGGL(k_decode_units, dim3((unsigned)unit_blocks), dim3(kDecT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_merge, dim3((unsigned)B * p.Hkv), dim3(kMergeT), 0, s, a);
+  hipLaunchKernelGGL(k_decode_merge, dim3((unsigned)B * p.Hkv), dim3(kMergeT), 0, s, a,
+                     unit_blocks * kDecWaves);
   return hipGetLastError();
 }
 
