@@ -46,7 +46,7 @@ class gp_config(ctypes.Structure):
         ("tau", ctypes.c_double), ("alpha_short", ctypes.c_float),
         ("alpha_long", ctypes.c_float), ("max_slots", ctypes.c_int32),
         ("policy", ctypes.c_int32), ("shrink_tau", ctypes.c_double),
-        ("min_tokens", ctypes.c_int32),
+        ("min_tokens", ctypes.c_int32), ("compact_workgroups", ctypes.c_int32),
     ]
 
 
@@ -178,6 +178,7 @@ class Config:
     policy: int = GP_POLICY_GROWPAGE
     shrink_tau: float = -0.005
     min_tokens: int = 1024
+    compact_workgroups: int = 0  # 0: 4 per CU
 
     @property
     def max_freed(self) -> int:
@@ -194,7 +195,8 @@ class Context:
         c = gp_config(cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                       cfg.page_size, cfg.recent_window, cfg.local_quota, cfg.p_num, cfg.p_den,
                       float(cfg.tau), float(cfg.alpha_short), float(cfg.alpha_long),
-                      cfg.max_slots, cfg.policy, float(cfg.shrink_tau), cfg.min_tokens)
+                      cfg.max_slots, cfg.policy, float(cfg.shrink_tau), cfg.min_tokens,
+                      cfg.compact_workgroups)
         h = ctypes.c_void_p()
         _check(L.gp_create(ctypes.byref(c), ctypes.byref(h)), "gp_create")
         self.handle = h

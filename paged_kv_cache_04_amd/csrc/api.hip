@@ -111,6 +111,8 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
   p.policy = cfg->policy;
   p.shrink_tau = cfg->shrink_tau;
   p.min_tokens = cfg->min_tokens;
+  p.compact_groups = cfg->compact_workgroups;
+  if (p.compact_groups < 0) return GP_ERR_INVALID_ARG;
   if (p.policy != GP_POLICY_GROWPAGE && p.policy != GP_POLICY_SHRINK) return GP_ERR_INVALID_ARG;
   if (p.policy == GP_POLICY_SHRINK &&
       (!(p.shrink_tau <= p.tau) || p.min_tokens < 0))
@@ -273,7 +275,10 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
     e = timed(c, GP_K_COMPACT, s, [&] {
       return gp::launch_compact(p, w, c->batch, action, pool->k_pool, pool->v_pool,
                                 pool->num_pages, bt->block_table, bt->max_pages, bt->num_tokens,
-                                shared, ws, c->d_err, s);
+                                shared,
+                                p.compact_groups > 0 ? p.compact_groups
+                                                     : c->num_cus * GP_COMPACT_BLOCKS_PER_CU,
+                                ws, c->d_err, s);
     });
   if (e == hipSuccess && (shrink || shared))
     e = timed(c, GP_K_RETURN, s, [&] {

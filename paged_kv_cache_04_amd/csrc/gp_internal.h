@@ -25,6 +25,10 @@ constexpr int64_t kMaxRequestTokens = int64_t(1) << 23;
 #define GP_DEMAND_BLOCKS_PER_CU 1
 #endif
 constexpr int kDemandBlocksPerCU = GP_DEMAND_BLOCKS_PER_CU;
+// Compaction: persistent workgroups per CU when the context sets no count.
+#ifndef GP_COMPACT_BLOCKS_PER_CU
+#define GP_COMPACT_BLOCKS_PER_CU 4
+#endif
 // Decode attention: persistent workgroups per CU of the unit kernel.
 #ifndef GP_DECODE_BLOCKS_PER_CU
 #define GP_DECODE_BLOCKS_PER_CU 2
@@ -43,6 +47,7 @@ struct Params {
   int policy;         // GP_POLICY_*
   double shrink_tau;  // Shrink threshold (GP_POLICY_SHRINK)
   int min_tokens;     // Shrink capacity floor
+  int compact_groups; // workgroups of the compaction kernel
   // pages of slots one event can free per request: 2 with Shrink, else 1
   int max_freed() const { return policy == GP_POLICY_SHRINK ? 2 : 1; }
 };
@@ -166,7 +171,7 @@ hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t
 hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
                           uint16_t* k_pool, uint16_t* v_pool, int pool_pages,
                           const int32_t* block_table, int max_pages, int32_t* num_tokens,
-                          bool shared, void* ws, int32_t* err, hipStream_t s);
+                          bool shared, int groups, void* ws, int32_t* err, hipStream_t s);
 
 hipError_t launch_return(const WsLayout& w, int B, int max_pages, int pool_pages,
                          int32_t* block_table, int32_t* num_pages, int32_t* free_stack,

@@ -16,7 +16,10 @@
 // it out of the caches leaves them to the next event's demand pass.  A chunk's stores land below every later
 // chunk's sources, and every earlier chunk has finished reading, so the
 // in-place move needs no copy of the row.  K and V rows, and different rows,
-// are disjoint and run as separate workgroups.
+// are disjoint items.  A persistent grid takes the items in the plan's
+// request order (longest first) with a stride of the grid; its size is a
+// context setting, so that compression on a second stream can leave CUs to
+// decoding (App. E.3).
 // Prefix-preserving compression (App. E.2): a shared page i of the request
 // has a target page, and destinations in page i are written there instead.
 // Sources stay in the old pages, which are only read, so the move is still
@@ -37,6 +40,8 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
                                                  int pool_pages,
                                                  const WsHeader* __restrict__ hdr,
                                                  const int64_t* __restrict__ page_off,
+                                                 const int32_t* __restrict__ req_order,
+                                                 int n_items,
                                                  const int8_t* __restrict__ action,
                                                  uint16_t* __restrict__ k_pool,
                                                  uint16_t* __restrict__ v_pool,
@@ -54,108 +59,125 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
   __shared__ int bad, first_new;
   if (!hdr->valid) return;
   const int LH = L * Hkv;
-  const int row = blockIdx.x >> 1, which = blockIdx.x & 1;
-  const int r = row / LH, lh = row % LH;
-  const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
-  if (act != GP_COMPRESS && act != GP_SHRINK) return;
-  if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
-  const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots freed
-  const int nd = m * b;                    // dropped slots
-  const int64_t P = page_off[r + 1] - page_off[r];
-  if (P < m + 1) return;
-  if (req_flags[r] & kReqBlocked) return;  // shared pages could not be replaced
-  const int l = lh / Hkv, h = lh % Hkv;
   const int t = threadIdx.x;
-  if (t == 0) {
-    bad = 0;
-    first_new = (int)P;
-  }
-  __syncthreads();
-  for (int k = t; k < nd; k += kCT) gap[k] = dropped[(int64_t)row * stride + k] - k;
-  for (int i = t; i < P; i += kCT) {
-    const int page = block_table[(int64_t)r * max_pages + i];
-    int dst = page;
-    if (target) {
-      const int tg = target[page_off[r] + i];
-      if (tg >= 0) {
-        dst = tg;
-        atomicMin(&first_new, i);
-      }
+  // one item: the K (which 0) or V (which 1) chain of row (r, lh); every
+  // value that steers a branch is workgroup-uniform and read into a scalar
+  auto item = [&](int r, int lh, int which) {
+    const int row = r * LH + lh;
+    const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+    if (act != GP_COMPRESS && act != GP_SHRINK) return;
+    if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
+    const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots freed
+    const int nd = m * b;                    // dropped slots
+    const int P = __builtin_amdgcn_readfirstlane((int)(page_off[r + 1] - page_off[r]));
+    if (P < m + 1) return;
+    if (__builtin_amdgcn_readfirstlane(req_flags[r]) & kReqBlocked) return;  // pages short
+    const int l = lh / Hkv, h = lh % Hkv;
+    if (t == 0) {
+      bad = 0;
+      first_new = P;
     }
-    if (page < 0 || page >= pool_pages || dst < 0 || dst >= pool_pages) bad = 1;
-    pg[i] = page;
-    pgd[i] = dst;
-  }
-  __syncthreads();
-  if (bad) {
-    if (t == 0) atomicOr(err, GP_DEVERR_PAGE);
-    return;
-  }
-  uint16_t* pool = which ? v_pool : k_pool;
-  // element offset of slot i of this row in physical page `page`
-  auto slot_base = [&](int page, int i) -> int64_t {
-    return (((int64_t)l * pool_pages + page) * Hkv + h) * (int64_t)(kPage * kD) +
-           (int64_t)(i & (kPage - 1)) * kD;
-  };
-  const int end = (int)((P - m) * b);
-  const int d0 = gap[0] > 0 ? gap[0] : 0;
-  const int start = first_new * b < d0 ? first_new * b : d0;
-  int par = 0;
-  for (int c0 = start; c0 < end; c0 += kRowsC, par ^= 1) {
-    // source and destination offsets of the chunk's destination rows,
-    // one binary search per thread (tables alternate between two buffers so
-    // the next chunk's tables never overwrite ones still being read)
-    {
-      const int drow = c0 + t;
-      if (t < kRowsC && drow < end) {
-        int lo = 0, hi = nd;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (gap[mid] <= drow) lo = mid + 1; else hi = mid;
+    __syncthreads();
+    for (int k = t; k < nd; k += kCT) gap[k] = dropped[(int64_t)row * stride + k] - k;
+    for (int i = t; i < P; i += kCT) {
+      const int page = block_table[(int64_t)r * max_pages + i];
+      int dst = page;
+      if (target) {
+        const int tg = target[page_off[r] + i];
+        if (tg >= 0) {
+          dst = tg;
+          atomicMin(&first_new, i);
         }
-        const int srow = drow + lo;
-        s_src[par][t] = slot_base(pg[srow >> 8], srow);
-        s_dst[par][t] = slot_base(pgd[drow >> 8], drow);
+      }
+      if (page < 0 || page >= pool_pages || dst < 0 || dst >= pool_pages) bad = 1;
+      pg[i] = page;
+      pgd[i] = dst;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(bad)) {
+      if (t == 0) atomicOr(err, GP_DEVERR_PAGE);
+      return;
+    }
+    uint16_t* pool = which ? v_pool : k_pool;
+    // element offset of slot i of this row in physical page `page`
+    auto slot_base = [&](int page, int i) -> int64_t {
+      return (((int64_t)l * pool_pages + page) * Hkv + h) * (int64_t)(kPage * kD) +
+             (int64_t)(i & (kPage - 1)) * kD;
+    };
+    const int end = (P - m) * b;
+    const int g0 = __builtin_amdgcn_readfirstlane(gap[0]);
+    const int fn = __builtin_amdgcn_readfirstlane(first_new);
+    const int d0 = g0 > 0 ? g0 : 0;
+    const int start = fn * b < d0 ? fn * b : d0;
+    int par = 0;
+    for (int c0 = start; c0 < end; c0 += kRowsC, par ^= 1) {
+      // source and destination offsets of the chunk's destination rows,
+      // one binary search per thread (tables alternate between two buffers
+      // so the next chunk's tables never overwrite ones still being read)
+      {
+        const int drow = c0 + t;
+        if (t < kRowsC && drow < end) {
+          int lo = 0, hi = nd;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (gap[mid] <= drow) lo = mid + 1; else hi = mid;
+          }
+          const int srow = drow + lo;
+          s_src[par][t] = slot_base(pg[srow >> 8], srow);
+          s_dst[par][t] = slot_base(pgd[drow >> 8], drow);
+        }
+      }
+      __syncthreads();
+      const int nrows = end - c0 < kRowsC ? end - c0 : kRowsC;
+      u32x4 v[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int piece = u * kCT + t;
+        const int ri = piece >> 4, part = piece & 15;
+        if (ri < nrows)
+          v[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(pool + s_src[par][ri] + part * 8));
+      }
+      // every source of this chunk must be read before any of its stores
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int piece = u * kCT + t;
+        const int ri = piece >> 4, part = piece & 15;
+        if (ri < nrows)
+          __builtin_nontemporal_store(v[u],
+                                      reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8));
       }
     }
-    __syncthreads();
-    const int nrows = end - c0 < kRowsC ? end - c0 : kRowsC;
-    u32x4 v[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int piece = u * kCT + t;
-      const int ri = piece >> 4, part = piece & 15;
-      if (ri < nrows)
-        v[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(pool + s_src[par][ri] + part * 8));
+    if (lh == 0 && which == 0 && t == 0) {
+      num_tokens[r] = end;
+      req_flags[r] = kReqCompacted;
     }
-    // every source of this chunk must be read before any of its stores
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int piece = u * kCT + t;
-      const int ri = piece >> 4, part = piece & 15;
-      if (ri < nrows)
-        __builtin_nontemporal_store(v[u],
-                                    reinterpret_cast<u32x4*>(pool + s_dst[par][ri] + part * 8));
-    }
-  }
-  if (lh == 0 && which == 0 && t == 0) {
-    num_tokens[r] = end;
-    req_flags[r] = kReqCompacted;
+  };
+  // items in the plan's request order (longest first), 2 LH per request,
+  // taken with a stride of the grid
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int r = __builtin_amdgcn_readfirstlane(req_order[it / (2 * LH)]);
+    const int rem = it % (2 * LH);
+    item(r, rem >> 1, rem & 1);
+    __syncthreads();  // the next item rewrites the LDS tables
   }
 }
 
 hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
                           uint16_t* k_pool, uint16_t* v_pool, int pool_pages,
                           const int32_t* block_table, int max_pages, int32_t* num_tokens,
-                          bool shared, void* ws, int32_t* err, hipStream_t s) {
+                          bool shared, int groups, void* ws, int32_t* err, hipStream_t s) {
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(k_compact, dim3((unsigned)(w.rows * 2)), dim3(kCT), 0, s, p.L, p.Hkv, p.b,
+  const int64_t n_items = w.rows * 2;
+  const int64_t grid = groups < n_items ? groups : n_items;
+  hipLaunchKernelGGL(k_compact, dim3((unsigned)grid), dim3(kCT), 0, s, p.L, p.Hkv, p.b,
                      p.b * p.max_freed(), pool_pages,
                      reinterpret_cast<const WsHeader*>(base + w.header),
-                     reinterpret_cast<const int64_t*>(base + w.page_off), action, k_pool, v_pool,
+                     reinterpret_cast<const int64_t*>(base + w.page_off),
+                     reinterpret_cast<const int32_t*>(base + w.req_order), (int)n_items, action,
+                     k_pool, v_pool,
                      block_table, max_pages, num_tokens,
                      reinterpret_cast<const int32_t*>(base + w.dropped),
                      shared ? reinterpret_cast<const int32_t*>(base + w.target) : nullptr,

@@ -95,3 +95,15 @@ class DecodeRunner:
 
     def device_errors(self) -> int:
         return gb.gp_get_device_errors(self.ctx)
+
+
+def sub_batch(batch: gb.Batch, rows) -> gb.Batch:
+    """A batch of the given request rows (device copies of their metadata;
+    the block tables still name the same pool pages)."""
+    idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=batch.block_table.device)
+    return gb.Batch(batch.block_table.index_select(0, idx).contiguous(),
+                    batch.num_pages.index_select(0, idx).contiguous(),
+                    batch.num_tokens.index_select(0, idx).contiguous(),
+                    batch.slot.index_select(0, idx).contiguous(),
+                    batch.position.index_select(0, idx).contiguous(),
+                    batch.num_pages.index_select(0, idx).cpu().numpy().astype(np.int32).copy())
