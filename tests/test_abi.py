@@ -42,6 +42,9 @@ def test_status_strings_and_invalid_config():
     assert lib.gp_create(ctypes.byref(bad4), ctypes.byref(h)) == 1  # unknown policy
     bad5 = gb.gp_config(2, 8, 2, 128, 256, 16, 64, 99, 100, 0.0, 0.1, 0.001, 8, 1, 0.01, 1024)
     assert lib.gp_create(ctypes.byref(bad5), ctypes.byref(h)) == 1  # shrink_tau > tau
+    bad6 = gb.gp_config(2, 8, 2, 128, 256, 16, 64, 99, 100, 0.0, 0.1, 0.001, 8, 0, -0.005, 1024,
+                        -1)
+    assert lib.gp_create(ctypes.byref(bad6), ctypes.byref(h)) == 1  # negative compaction grid
     assert not h.value
 
 
