@@ -17,7 +17,11 @@
  *  - Asynchrony: every gp_* call that takes a stream enqueues kernels on it
  *    and returns after host-side validation; results are valid once the
  *    stream has reached that point.  No call synchronises the device except
- *    gp_get_counters, gp_get_device_errors and gp_profile_read.
+ *    gp_get_counters, gp_get_device_errors and gp_profile_read.  The event
+ *    calls (gp_update_summaries, gp_demand, gp_grow_page, gp_compress_hold,
+ *    gp_decode_attention) enqueue kernels only (no allocation, memset or
+ *    copy), so a caller may capture them in a HIP graph; the host-side
+ *    validation then runs once, at capture time.
  *  - Errors: host-checkable problems return an error status and enqueue
  *    nothing.  Device-side checks (out-of-range slot, position or page id,
  *    a compress request with fewer than 2 pages) never fault: the offending
