@@ -13,9 +13,9 @@
 // in 512-row chunks (128 KiB, 16 pieces of 16 bytes per thread): it loads a
 // whole chunk into registers, waits for the loads and barriers, then stores.
 // Loads and stores are non-temporal: each byte is touched once, and keeping
-// it out of the caches leaves them to the next event's demand pass.  A chunk's stores land below every later
-// chunk's sources, and every earlier chunk has finished reading, so the
-// in-place move needs no copy of the row.  K and V rows, and different rows,
+// it out of the caches leaves them to the next event's demand pass.  A
+// chunk's stores land below every later chunk's sources, and every earlier
+// chunk has finished reading, so the in-place move needs no copy of the row.  K and V rows, and different rows,
 // are disjoint items.  A persistent grid takes the items in the plan's
 // request order (longest first) with a stride of the grid; its size is a
 // context setting, so that compression on a second stream can leave CUs to

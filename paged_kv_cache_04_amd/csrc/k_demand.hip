@@ -5,9 +5,11 @@
 // Reasoning Serving" (arXiv 2609.03494): §3.1 Eq. 2, §3.2 Eq. 7, §3.3 Eq. 9,
 // App. E.1 ("Demand estimation at capacity boundaries").
 //
-// Persistent kernel, two 8-wave workgroups per CU (one can stream keys while
-// the other works on its row's distributions).  Workgroups pull rows from
-// a queue ordered longest request first.  Per row:
+// Persistent kernel, kDemandBlocksPerCU workgroups of 16 / kDemandBlocksPerCU
+// waves per CU (one 16-wave workgroup by default: two 8-wave workgroups, one
+// streaming keys while the other works on its row's distributions, measured
+// no faster).  Workgroups pull rows from a queue ordered longest request
+// first.  Per row:
 //  1. score: each wave takes every 16th 64-key tile of the row and pipelines
 //     it in two halves (key elements 0-63, then 64-127): while it multiplies
 //     one half from its private LDS stage (half rows padded to 144 B so the
