@@ -14,8 +14,11 @@ rule over the request's own D_p values (tau = 0), pages go to the Grow
 requests in request order from the top of the free stack while the pool
 lasts and the rest fall back (§3.2, App. E.2), every compressing request
 ends one page of slots shorter and every growing request keeps its bytes.
-Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
-Reasoning Serving"."""
+The decode step over the same batch (all 32 layers, as the benchmark runs
+it) is checked the same way: sampled (request, layer, KV head) outputs
+against the fp64 definition of §3.1 Eq. 3, and the summaries it updates on
+the sampled layers bit for bit against A0.  Citations are to "GrowPage:
+On-Demand KV Budgeting for Efficient LLM Reasoning Serving"."""
 import dataclasses
 import gc
 
@@ -25,6 +28,7 @@ import torch
 
 import oracle
 from paged_kv_cache_04_amd import synth
+from paged_kv_cache_04_amd.runner import DecodeRunner
 from gpu_util import device_rows, gb_config, log, oracle_config, run_stream_gpu, runner_for
 
 pytestmark = pytest.mark.gpu
@@ -149,5 +153,73 @@ def test_batch64_full_size_sampled_rows():
         assert np.array_equal(kg, kw[:n]) and np.array_equal(vg, vw[:n]), (r, l, h)
     log(f"  {len(sample)} rows match ({n_comp} compacted)")
     del run, wl, pre
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+DEC_TOL = 1e-3  # of the row's largest |v|: fp32 arithmetic, hardware exp2
+
+
+@needs_gpu
+def test_batch64_decode_sampled_heads():
+    log("test_batch64_decode_sampled_heads")
+    gc.collect()
+    torch.cuda.empty_cache()
+    wl = synth.batch64("cuda", pool_pages=POOL_PAGES)
+    s = wl.shape
+    G = s.Hq // s.Hkv
+    cfg = gb_config(s, max_slots=wl.max_slots)
+    ocfg = oracle_config(cfg)
+    B = wl.B
+    bt = wl.block_table.cpu().numpy()
+    P = wl.num_pages.cpu().numpy().astype(np.int64)
+    slot = wl.slot.cpu().numpy()
+    pos = wl.position.cpu().numpy()
+    rope = wl.rope.cpu().numpy()
+    rng = np.random.default_rng(6465)
+    layers = np.sort(rng.choice(s.L, SAMPLE_LAYERS, replace=False))
+    sample = [(r, int(rng.choice(layers)), int(rng.integers(s.Hkv)))
+              for r in range(B) for _ in range(ROWS_PER_REQUEST)]
+
+    # summaries up to the decode step, then one decode step of every layer
+    run = runner_for(wl, cfg, want_abar=False, want_dropped=False)
+    run_stream_gpu(run, wl, steps=wl.steps - 1)
+    q = wl.query(wl.steps - 1)
+    no_first = torch.zeros(B, dtype=torch.uint8, device="cuda")
+    dec = DecodeRunner(cfg, run.pool, run.batch, wl.rope)
+    outs = {}
+    for l in range(s.L):
+        o = dec.layer(l, q[:, l].contiguous(), run.qstate, no_first)
+        if l in layers:
+            outs[l] = o.cpu().numpy().copy()
+    torch.cuda.synchronize()
+    assert dec.device_errors() == 0
+
+    # A0 on the sampled layers: the stream, then the decode step's update
+    ocfg_s = dataclasses.replace(ocfg, L=SAMPLE_LAYERS)
+    state = np.zeros((SAMPLE_LAYERS, wl.max_slots, 2, s.Hq, s.d), np.float32)
+    lidx = torch.as_tensor(layers, device="cuda")
+    for t in range(wl.steps):
+        first = wl.first_step(t).cpu().numpy() if t < wl.steps - 1 else no_first.cpu().numpy()
+        oracle.ema(ocfg_s, state, wl.query(t).index_select(1, lidx).cpu().numpy(), slot, first)
+    got_state = run.qstate.index_select(0, lidx).cpu().numpy()
+    assert np.array_equal(got_state.view(np.uint32), state.view(np.uint32))
+
+    qn = q.index_select(1, lidx).cpu().numpy()
+    worst = 0.0
+    for r, l, h in sample:
+        pages = bt[r, :P[r]]
+        keys = device_rows(wl.k_pool, l, h, pages)
+        vals = device_rows(wl.v_pool, l, h, pages)
+        li = int(np.searchsorted(layers, l))
+        want, _ = oracle.decode_attention_f64(qn[r, li, h * G:(h + 1) * G], keys, vals,
+                                              rope[int(pos[r])])
+        vmax = np.abs(oracle.bf16_to_f64(vals)).max()
+        err = np.abs(outs[l][r, h * G:(h + 1) * G].astype(np.float64) - want).max() / vmax
+        worst = max(worst, err)
+        assert err <= DEC_TOL, (r, l, h, err)
+    log(f"  {len(sample)} sampled heads, worst error / max|v| = {worst:.2e}; summaries of "
+        f"layers {layers.tolist()} bit-exact")
+    del run, dec, wl
     gc.collect()
     torch.cuda.empty_cache()
