@@ -39,6 +39,24 @@ def test_ragged_batch_mixed_actions(seed):
 
 
 @needs_gpu
+def test_longest_compressible_rows():
+    """Rows at the largest size Compress & Hold takes (256 pages, 65536
+    tokens) and one of 160 pages: their candidates exceed what the selection
+    holds in LDS, so it runs on the importance array in HBM, the demand
+    kernel's logits ring holds 65536 tokens, and compaction walks 256-page
+    chains; a 2-page request in the same batch takes the LDS path.  Every
+    output against the oracle."""
+    log("test_longest_compressible_rows")
+    P = [256, 160, 2]
+    wl = synth.make_workload(SMALL, P, sum(P) + 4, seed=1300, device="cuda",
+                             align=["S", "L", "S"], cluster_sizes=[200, 60, 8], free_pages=0,
+                             steps=120, short_steps=16, max_slots=4)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    ref = check_event(wl, cfg, check_f64=False)
+    assert (ref["action"] == 0).all()
+
+
+@needs_gpu
 def test_single_page_request_grows_and_cannot_compress():
     """A request of one page has no historical candidates: it is given Grow
     with Delta = 0; with the pool empty it falls back, and compressing it is
