@@ -30,7 +30,8 @@
 //     view histogrammed in LDS with counts and masses floor(abar * 2^40);
 //  4. D_p per view: the bucket where the descending prefix mass reaches p,
 //     then the remaining 20 bits resolved on that bucket's members only
-//     (collected into LDS, or scanned in the key ring when too many), then
+//     (collected into LDS, or scanned in the key ring when too many; both
+//     views in the same two passes), then
 //     D_p = (count above) + ceil(remaining mass / member mass).
 #include "gp_internal.h"
 
@@ -46,7 +47,7 @@ constexpr int kWaveStage = 64 * kHalfPad;     // bytes per wave
 constexpr int kLdsBytes = kDW * kWaveStage;   // 147456, reused after scoring
 constexpr int kH1 = 2048;                     // first-digit buckets
 constexpr int kH2 = 1024;                     // second/third-digit buckets
-constexpr int kListCap = (kLdsBytes - 2 * kH1 * 8 - kH2 * 12) / 4;  // boundary members in LDS
+constexpr int kListCap = (kLdsBytes - 2 * kH1 * 8 - 2 * kH2 * 12) / 4;  // boundary members in LDS
 constexpr int kListHalf = kListCap / 2;                            // per view
 
 // acc[qi] += q[qi][e] * k[e] for e = 0..3 in order (4 bf16 keys in k).
@@ -241,9 +242,9 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
   unsigned char* my = lds + w * kWaveStage;
   // LDS views used after scoring
   double* h1m = reinterpret_cast<double*>(lds);                              // [2][kH1]
-  uint32_t* h2c = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 8);            // [kH2]
-  uint64_t* h2m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 8 + kH2 * 4);  // [kH2]
-  uint32_t* list = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 8 + kH2 * 12);  // [kListCap]
+  uint32_t* h2c = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 8);                // [2][kH2]
+  uint64_t* h2m = reinterpret_cast<uint64_t*>(lds + 2 * kH1 * 8 + 2 * kH2 * 4);  // [2][kH2]
+  uint32_t* list = reinterpret_cast<uint32_t*>(lds + 2 * kH1 * 8 + 2 * kH2 * 12);  // [kListCap]
 
   while (true) {
     if (t == 0) s_item = atomicAdd(a.row_counter, 1);
@@ -549,65 +550,76 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
       }
     }
     __syncthreads();
-    for (int x = 0; x < 2; ++x) {
-      int32_t* outp = x == 0 ? a.k_short : a.k_long;
-      const uint64_t target = s_W[x] * (uint64_t)a.p_num;
-      const uint32_t* lst = list + x * kListHalf;
-      const bool in_lds = s_list_n[x] <= kListHalf;
-      uint32_t prefix = (uint32_t)s_dig[x] << 20;
-      // digits 2 (bits 19..10) and 3 (bits 9..0) over the bucket's members
+    // digits 2 (bits 19..10) and 3 (bits 9..0) over each view's boundary
+    // members, both views in the same passes (each into its own counts and
+    // masses; waves 0 and 1 then scan one view each)
+    {
+      const bool in_lds0 = s_list_n[0] <= kListHalf, in_lds1 = s_list_n[1] <= kListHalf;
+      uint32_t prefix0 = (uint32_t)s_dig[0] << 20, prefix1 = (uint32_t)s_dig[1] << 20;
       for (int pass = 0; pass < 2; ++pass) {
         const int shift = pass == 0 ? 10 : 0;
         const uint32_t mask = pass == 0 ? 0xfff00000u : 0xfffffc00u;
-        for (int k = t; k < kH2; k += kDT) {
+        for (int k = t; k < 2 * kH2; k += kDT) {
           h2c[k] = 0;
           h2m[k] = 0;
         }
         __syncthreads();
-        if (in_lds) {
-          const int n = s_list_n[x];
-          for (int k = t; k < n; k += kDT) {
-            const uint32_t key = lst[k];
-            if ((key & mask) == prefix) {
-              const uint32_t dig = (key >> shift) & (kH2 - 1);
-              atomicAdd(&h2c[dig], 1u);
-              atomicAdd((unsigned long long*)&h2m[dig],
-                        (unsigned long long)fix40(__uint_as_float(key)));
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t prefix = x == 0 ? prefix0 : prefix1;
+          uint32_t* hc = h2c + x * kH2;
+          uint64_t* hm = h2m + x * kH2;
+          if (x == 0 ? in_lds0 : in_lds1) {
+            const uint32_t* lst = list + x * kListHalf;
+            const int n = s_list_n[x];
+            for (int k = t; k < n; k += kDT) {
+              const uint32_t key = lst[k];
+              if ((key & mask) == prefix) {
+                const uint32_t dig = (key >> shift) & (kH2 - 1);
+                atomicAdd(&hc[dig], 1u);
+                atomicAdd((unsigned long long*)&hm[dig],
+                          (unsigned long long)fix40(__uint_as_float(key)));
+              }
             }
-          }
-        } else {
-          for (int64_t i = t; i < ndem; i += kDT) {
-            const uint32_t key = __float_as_uint(rk[i * 2 + x]);
-            if ((key & mask) == prefix) {
-              const uint32_t dig = (key >> shift) & (kH2 - 1);
-              atomicAdd(&h2c[dig], 1u);
-              atomicAdd((unsigned long long*)&h2m[dig],
-                        (unsigned long long)fix40(__uint_as_float(key)));
+          } else {
+            for (int64_t i = t; i < ndem; i += kDT) {
+              const uint32_t key = __float_as_uint(rk[i * 2 + x]);
+              if ((key & mask) == prefix) {
+                const uint32_t dig = (key >> shift) & (kH2 - 1);
+                atomicAdd(&hc[dig], 1u);
+                atomicAdd((unsigned long long*)&hm[dig],
+                          (unsigned long long)fix40(__uint_as_float(key)));
+              }
             }
           }
         }
         __syncthreads();
-        if (w == 0) {
-          uint64_t mab = s_mab[x];
-          uint32_t cab = s_cab[x];
+        if (w < 2) {
+          uint64_t mab = s_mab[w];
+          uint32_t cab = s_cab[w];
           int dd;
-          scan_desc<kH2>(h2c, h2m, target, (uint32_t)a.p_den, mab, cab, dd);
+          scan_desc<kH2>(h2c + w * kH2, h2m + w * kH2, s_W[w] * (uint64_t)a.p_num,
+                         (uint32_t)a.p_den, mab, cab, dd);
           if (lane == 0) {
-            s_dig[x] = dd;
-            s_mab[x] = mab;
-            s_cab[x] = cab;
+            s_dig[w] = dd;
+            s_mab[w] = mab;
+            s_cab[w] = cab;
           }
         }
         __syncthreads();
-        prefix |= (uint32_t)s_dig[x] << shift;
+        prefix0 |= (uint32_t)s_dig[0] << shift;
+        prefix1 |= (uint32_t)s_dig[1] << shift;
       }
-      if (t == 0) {
+      if (t < 2) {
+        int32_t* outp = t == 0 ? a.k_short : a.k_long;
+        const uint32_t prefix = t == 0 ? prefix0 : prefix1;
+        const uint64_t target = s_W[t] * (uint64_t)a.p_num;
         const bool has = ndem > 0;
         const uint64_t wt = fix40(__uint_as_float(has ? prefix : 0u));
-        const uint64_t need = target - s_mab[x] * (uint64_t)a.p_den;
+        const uint64_t need = target - s_mab[t] * (uint64_t)a.p_den;
         const uint64_t den = wt * (uint64_t)a.p_den;
         const uint64_t rest = den != 0 ? (need + den - 1) / den : 0;
-        outp[row] = has ? (int32_t)(s_cab[x] + rest) : 0;
+        outp[row] = has ? (int32_t)(s_cab[t] + rest) : 0;
       }
       __syncthreads();
     }
