@@ -29,7 +29,9 @@
  *    read with gp_get_device_errors.  A failed HIP launch returns GP_ERR_HIP.
  *  - Threads: one context per host thread.
  *  - Data types: fp32 for queries and query states, bf16 (raw uint16 bits)
- *    for keys and values, int32 for ids and counts.
+ *    for keys and values, int32 for ids and counts.  Device buffers start on
+ *    16-byte boundaries (the kernels read and write 16-byte vectors; torch
+ *    allocations are aligned far beyond that).
  *
  * Layouts (row-major, outermost first)
  *  - K and V pools: [L][num_pages][Hkv][b][d] bf16.  A page id is shared by

@@ -168,26 +168,55 @@ __global__ __launch_bounds__(256) void k_qhat(const float* __restrict__ qstate,
     if (t == 0) atomicOr(err, GP_DEVERR_POSITION);
     pos = pos < 0 ? 0 : rope_rows - 1;
   }
-  const float* qt = qcur + (((int64_t)r * L + l) * Hq + hq) * kD;
-  const float* qb = qstate + ((((int64_t)l * M + s) * 2 + x) * Hq + hq) * kD;
+  // both vectors are read with 16-byte loads, all issued before the serial
+  // sums of squares run over them in index order
+  const float4* qt = reinterpret_cast<const float4*>(qcur + (((int64_t)r * L + l) * Hq + hq) * kD);
+  const float4* qb =
+      reinterpret_cast<const float4*>(qstate + ((((int64_t)l * M + s) * 2 + x) * Hq + hq) * kD);
+  float4 tv[kD / 4], bv[kD / 4];
+#pragma unroll
+  for (int i = 0; i < kD / 4; ++i) {
+    tv[i] = qt[i];
+    bv[i] = qb[i];
+  }
   float ssq = 0.0f, ssx = 0.0f;
-  for (int j = 0; j < kD; ++j) ssq = __builtin_fmaf(qt[j], qt[j], ssq);
-  for (int j = 0; j < kD; ++j) ssx = __builtin_fmaf(qb[j], qb[j], ssx);
+#pragma unroll
+  for (int i = 0; i < kD / 4; ++i) {
+    ssq = __builtin_fmaf(tv[i].x, tv[i].x, ssq);
+    ssq = __builtin_fmaf(tv[i].y, tv[i].y, ssq);
+    ssq = __builtin_fmaf(tv[i].z, tv[i].z, ssq);
+    ssq = __builtin_fmaf(tv[i].w, tv[i].w, ssq);
+  }
+#pragma unroll
+  for (int i = 0; i < kD / 4; ++i) {
+    ssx = __builtin_fmaf(bv[i].x, bv[i].x, ssx);
+    ssx = __builtin_fmaf(bv[i].y, bv[i].y, ssx);
+    ssx = __builtin_fmaf(bv[i].z, bv[i].z, ssx);
+    ssx = __builtin_fmaf(bv[i].w, bv[i].w, ssx);
+  }
   float gamma = ssx > 0.0f ? __builtin_sqrtf(ssq / ssx) : 0.0f;
   if (zero) gamma = 0.0f;
   const float scale = 1.0f / __builtin_sqrtf((float)kD);
-  const float* cs = rope + (int64_t)pos * kD;
+  const float4* cs = reinterpret_cast<const float4*>(rope + (int64_t)pos * kD);
   const int kvh = hq / kGroup, qi = x * kGroup + hq % kGroup;
   float* out = qhat + (((int64_t)r * L + l) * Hkv + kvh) * (kNQ * kD);
-  constexpr int half = kD / 2;
-  for (int j = 0; j < half; ++j) {
-    const float a = gamma * qb[j], c2 = gamma * qb[j + half];
-    const float c = cs[j], sn = cs[half + j];
-    const float y1 = __builtin_fmaf(a, c, -(c2 * sn));
-    const float y2 = __builtin_fmaf(c2, c, a * sn);
-    const int j2 = j + half;
-    out[(j / 4) * 32 + qi * 4 + (j % 4)] = y1 * scale;
-    out[(j2 / 4) * 32 + qi * 4 + (j2 % 4)] = y2 * scale;
+  // element j of the first half pairs with j + d/2; quad i holds j = 4i .. 4i+3
+  constexpr int hq4 = kD / 8;  // quads per half
+  auto rot = [&](float b1, float b2, float c, float sn, float& y1, float& y2) {
+    const float a = gamma * b1, c2 = gamma * b2;
+    y1 = __builtin_fmaf(a, c, -(c2 * sn)) * scale;
+    y2 = __builtin_fmaf(c2, c, a * sn) * scale;
+  };
+#pragma unroll
+  for (int i = 0; i < hq4; ++i) {
+    const float4 c = cs[i], sn = cs[hq4 + i], b1 = bv[i], b2 = bv[hq4 + i];
+    float4 y1, y2;
+    rot(b1.x, b2.x, c.x, sn.x, y1.x, y2.x);
+    rot(b1.y, b2.y, c.y, sn.y, y1.y, y2.y);
+    rot(b1.z, b2.z, c.z, sn.z, y1.z, y2.z);
+    rot(b1.w, b2.w, c.w, sn.w, y1.w, y2.w);
+    *reinterpret_cast<float4*>(out + i * 32 + qi * 4) = y1;
+    *reinterpret_cast<float4*>(out + (hq4 + i) * 32 + qi * 4) = y2;
   }
 }
 
