@@ -171,3 +171,40 @@ def row_offsets(P: np.ndarray, L: int, Hkv: int, b: int):
                 offs[(r, l, h)] = (o, N)
                 o += N
     return offs
+
+
+def check_decode_after_event(wl, cfg, hc: HostCopy, ref: dict, seed: int, tol: float = 1e-3):
+    """One decode step over the cache an event left (block tables, page
+    counts and token counts as the GPU event wrote them), every (request,
+    layer, KV head) against the fp64 definition of §3.1 Eq. 3 over the
+    oracle's rows: its compacted K/V for a request that compressed (freed
+    pages of slots), the original rows otherwise.  Returns the worst error
+    relative to the row's largest |v|."""
+    from paged_kv_cache_04_amd.runner import DecodeRunner
+    s = wl.shape
+    G = s.Hq // s.Hkv
+    pool = gb.Pool(wl.k_pool, wl.v_pool, wl.free_stack, wl.free_count)
+    batch = gb.Batch(wl.block_table, wl.num_pages, wl.num_tokens, wl.slot, wl.position,
+                     wl.num_pages.cpu().numpy().astype(np.int32).copy())
+    dec = DecodeRunner(cfg, pool, batch, wl.rope)
+    q = torch.randn((wl.B, s.L, s.Hq, s.d), dtype=torch.float32, device=wl.device,
+                    generator=torch.Generator(wl.device).manual_seed(seed))
+    outs = [dec.layer(l, q[:, l].contiguous()).cpu().numpy().copy() for l in range(s.L)]
+    assert dec.device_errors() == 0
+    qn = q.cpu().numpy()
+    worst = 0.0
+    for r in range(wl.B):
+        pages = hc.bt[r, :hc.P[r]]
+        for l in range(s.L):
+            for h in range(s.Hkv):
+                if ref["freed"][r] > 0:
+                    keys, vals = ref["compacted"][(r, l, h)]
+                else:
+                    keys, vals = hc.keys(l, h, pages), hc.values(l, h, pages)
+                want, _ = oracle.decode_attention_f64(qn[r, l, h * G:(h + 1) * G], keys, vals,
+                                                      hc.rope[int(hc.pos[r])])
+                vmax = np.abs(oracle.bf16_to_f64(vals)).max()
+                err = np.abs(outs[l][r, h * G:(h + 1) * G].astype(np.float64) - want).max() / vmax
+                worst = max(worst, err)
+                assert err <= tol, (r, l, h, err)
+    return worst

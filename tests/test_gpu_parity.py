@@ -2,14 +2,16 @@
 edge cases, and the full-size single-request Llama-8B configuration, each
 compared element by element with the oracle (bit-exact for D_p, decisions,
 grants, dropped slots and compacted K/V bytes; bit-exact and within 1e-3 of
-fp64 for the fp32 distributions)."""
+fp64 for the fp32 distributions); after a Shrink batch, the next decode
+step over the changed caches against the fp64 definition."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from paged_kv_cache_04_amd import synth
-from gpu_util import device_rows, gb_config, log, run_stream_gpu, runner_for
+from gpu_util import (HostCopy, check_decode_after_event, device_rows, gb_config, log,
+                      run_stream_gpu, runner_for)
 from test_gpu_tiny import check_event
 
 pytestmark = pytest.mark.gpu
@@ -142,11 +144,15 @@ def test_shrink_policy_batch():
                              cluster_sizes=[30, 60, 30, 30, 30, 30, 30], free_pages=2,
                              steps=120, short_steps=16, max_slots=8)
     cfg = gb_config(wl.shape, max_slots=wl.max_slots, policy=1)
+    hc = HostCopy(wl)
     ref = check_event(wl, cfg, check_f64=False)
     act = list(ref["action"])
     log(f"  actions {act}, decisions {list(ref['dem']['decision'])}")
     assert act.count(2) >= 2 and act[3] == 0  # P = 4 is at the capacity floor
     assert ref["shrunk"] == act.count(2)
+    # the next decode step reads the shrunk, compacted and grown caches
+    worst = check_decode_after_event(wl, cfg, hc, ref, seed=4244)
+    log(f"  decode after the event: worst error / max|v| = {worst:.2e}")
 
 
 @needs_gpu

@@ -7,14 +7,15 @@ read through the new block tables), plus: the target pages taken from the
 free stack, the all-or-nothing rule in request order when pages run short,
 the reference counts after the release, the bytes of every page that was
 shared before the event (never written), and Shrink's handling of a shared
-last page."""
+last page; after the mixed batch, the next decode step reads the compacted
+rows through the new block tables."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from paged_kv_cache_04_amd import synth
-from gpu_util import gb_config, log
+from gpu_util import HostCopy, check_decode_after_event, gb_config, log
 from test_gpu_tiny import check_event
 
 pytestmark = pytest.mark.gpu
@@ -64,11 +65,15 @@ def test_prefix_sharing_mixed_batch():
     bt0 = wl.block_table.cpu().numpy()
     rc = share_prefixes(wl, [(1, 0, 3), (2, 0, 2), (4, 3, 4)], cache_refs=[int(bt0[3, 0])])
     cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    hc = HostCopy(wl)
     ref = check_event(wl, cfg, check_f64=False, refcount=rc)
     log(f"  actions {list(ref['action'])}, target pages {ref['copied']}")
     assert ref["ok"].all()
     compressing = [r for r in range(len(P)) if ref["action"][r] == oracle.COMPRESS]
     assert len(set(compressing) & {0, 1, 2, 3, 4}) >= 3 and ref["copied"] >= 6
+    # the next decode step reads the compacted rows through the target pages
+    worst = check_decode_after_event(wl, cfg, hc, ref, seed=5151)
+    log(f"  decode after the event: worst error / max|v| = {worst:.2e}")
 
 
 @needs_gpu
