@@ -1,7 +1,10 @@
 """Error paths on the GPU, each forced from the host with inputs that the
 kernels' own checks catch (every kernel still runs to completion and no
 access leaves its buffers): the device error bits are set and the pool is left
-as it was where the event cannot proceed."""
+as it was where the event cannot proceed.  Calls that host-side validation
+refuses return an error status and enqueue nothing.  The in-place
+compaction's only ordering hazard is checked by running it with several
+persistent grid sizes (a different workgroup-to-item order each)."""
 import numpy as np
 import pytest
 import torch
@@ -91,3 +94,84 @@ def test_stale_host_page_counts():
     assert run.device_errors() & ERR_PAGES
     assert (run.out.k_short == -7).all()
     assert np.array_equal(device_rows(wl.k_pool, 0, 0, pages), k_before)
+
+
+@needs_gpu
+def test_host_validation_errors():
+    """Calls that host-side validation refuses return an error status and
+    enqueue nothing: a workspace smaller than gp_workspace_bytes, Compress &
+    Hold without the preceding gp_demand on that workspace (or with another
+    workspace), a decode workspace smaller than gp_decode_workspace_bytes,
+    a layer outside the model; the pool, token counts and outputs keep
+    their contents."""
+    log("test_host_validation_errors")
+    wl = _workload(44)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    torch.cuda.synchronize()
+    pages = wl.block_table[1, :3].cpu().numpy().copy()
+    k_before = device_rows(wl.k_pool, 0, 0, pages)
+    nt_before = wl.num_tokens.clone()
+    run.out.k_short.fill_(-7)
+    small = torch.empty(run.ws.numel() - 256, dtype=torch.uint8, device="cuda")
+
+    def refused(fn, what):
+        with pytest.raises(gb.GPError, match=what):
+            fn()
+
+    refused(lambda: gb.gp_demand(run.ctx, run.pool, run.batch, run.qstate, q, run.rope, small,
+                                 run.out), "workspace")
+    # no gp_demand has prepared this context's workspace yet
+    refused(lambda: gb.gp_compress_hold(run.ctx, run.pool, run.batch, None, run.ws), "workspace")
+    run.demand(q)
+    other = torch.empty_like(run.ws)
+    refused(lambda: gb.gp_compress_hold(run.ctx, run.pool, run.batch, None, other), "workspace")
+    torch.cuda.synchronize()
+    assert (run.out.k_short != -7).all()  # the accepted gp_demand ran
+    assert np.array_equal(device_rows(wl.k_pool, 0, 0, pages), k_before)
+    assert torch.equal(wl.num_tokens, nt_before)
+    # decode: workspace and layer checks
+    total_pages = int(run.batch.num_pages_host.sum())
+    need = gb.gp_decode_workspace_bytes(run.ctx, wl.B, total_pages)
+    out = torch.zeros((wl.B, wl.shape.Hq, wl.shape.d), dtype=torch.float32, device="cuda")
+    q0 = q[:, 0].contiguous()
+    refused(lambda: gb.gp_decode_attention(
+        run.ctx, run.pool, run.batch, 0, q0, None, None, run.rope, out,
+        torch.empty(need - 256, dtype=torch.uint8, device="cuda")), "workspace")
+    refused(lambda: gb.gp_decode_attention(
+        run.ctx, run.pool, run.batch, wl.shape.L, q0, None, None, run.rope, out,
+        torch.empty(need, dtype=torch.uint8, device="cuda")), "invalid argument")
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    assert run.device_errors() == 0
+
+
+@needs_gpu
+@pytest.mark.parametrize("groups", [1, 3, 64])
+def test_compaction_grid_sizes_give_identical_bytes(groups):
+    """The compaction's persistent grid takes its (row, K/V) items in a
+    different workgroup order for every grid size; in-place compaction must
+    not depend on it: the pool, token counts and dropped slots are bitwise
+    those of the default grid."""
+    log(f"test_compaction_grid_sizes_give_identical_bytes[{groups}]")
+    P = [7, 3, 9, 5, 4]
+    results = []
+    for g in (0, groups):
+        wl = synth.make_workload(SMALL, P, 40, seed=4500, device="cuda",
+                                 align=["S", "S", "L", "S", "S"], cluster_sizes=[40] * 5,
+                                 free_pages=0, steps=80, short_steps=16, max_slots=8)
+        cfg = gb_config(wl.shape, max_slots=wl.max_slots, compact_workgroups=g)
+        run = runner_for(wl, cfg)
+        q = run_stream_gpu(run, wl)
+        run.event(q)
+        torch.cuda.synchronize()
+        assert run.device_errors() == 0
+        bt = wl.block_table.cpu().numpy()
+        used = torch.as_tensor(np.unique(bt[bt >= 0]), device="cuda")
+        results.append((wl.k_pool[:, used].view(torch.int16).clone(),
+                        wl.v_pool[:, used].view(torch.int16).clone(),
+                        wl.num_tokens.clone(), run.dropped.clone()))
+        del run, wl
+    for a, b in zip(results[0], results[1]):
+        assert torch.equal(a, b)
