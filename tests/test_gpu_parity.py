@@ -108,6 +108,25 @@ def test_constant_keys_all_ties():
 
 
 @needs_gpu
+def test_constant_keys_long_rows():
+    """All keys equal on rows of 64 and 130 pages: every candidate of a view
+    falls in one first-digit bucket, more than the demand kernel keeps in
+    LDS, so D_p is resolved by scanning its key ring; the 130-page rows also
+    run the selection's ties on the HBM path.  Every output against the
+    oracle; D_p = ceil(p |C_t|)."""
+    log("test_constant_keys_long_rows")
+    P = [64, 130]
+    wl = synth.make_workload(SMALL, P, sum(P) + 4, seed=6, device="cuda", align=[None, None],
+                             free_pages=0, steps=40, short_steps=8, max_slots=4)
+    wl.k_pool.fill_(0.5)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    ref = check_event(wl, cfg, check_f64=False)
+    for r, p in enumerate(P):
+        want = int(np.ceil(0.99 * (p - 1) * 256))
+        assert (ref["dem"]["ks"][r] == want).all() and (ref["dem"]["kl"][r] == want).all()
+
+
+@needs_gpu
 def test_max_batch_1024_requests():
     """The largest batch the library takes (1024 requests), short ragged
     requests of 2-4 pages, a few free pages so that some Grow decisions are
