@@ -41,21 +41,28 @@ def test_ragged_batch_mixed_actions(seed):
 
 
 @needs_gpu
-def test_longest_compressible_rows():
+@pytest.mark.parametrize("policy", [0, 1])
+def test_longest_compressible_rows(policy):
     """Rows at the largest size Compress & Hold takes (256 pages, 65536
     tokens) and one of 160 pages: their candidates exceed what the selection
     holds in LDS, so it runs on the importance array in HBM, the demand
     kernel's logits ring holds 65536 tokens, and compaction walks 256-page
-    chains; a 2-page request in the same batch takes the LDS path.  Every
-    output against the oracle."""
-    log("test_longest_compressible_rows")
+    chains; a 2-page request in the same batch takes the LDS path.  Under
+    GrowPage-Shrink the short-view requests shrink (2b drops on the HBM
+    path, a page returned).  Every output against the oracle."""
+    log(f"test_longest_compressible_rows[{policy}]")
     P = [256, 160, 2]
     wl = synth.make_workload(SMALL, P, sum(P) + 4, seed=1300, device="cuda",
                              align=["S", "L", "S"], cluster_sizes=[200, 60, 8], free_pages=0,
                              steps=120, short_steps=16, max_slots=4)
-    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots, policy=policy)
     ref = check_event(wl, cfg, check_f64=False)
-    assert (ref["action"] == 0).all()
+    act = list(ref["action"])
+    log(f"  actions {act}")
+    if policy == 0:
+        assert act == [0, 0, 0]
+    else:
+        assert act[0] == 2 and act[1] == 0 and ref["shrunk"] >= 1
 
 
 @needs_gpu
