@@ -152,9 +152,12 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
+// The logits ring holds, per 64-key tile, the first four logits of its keys
+// and then the last four ([tile][2][64][4] floats), so that each store
+// instruction of the scoring loop writes 1 KiB contiguously.
 __device__ __forceinline__ void load_logits8(const float* lg, int64_t i, float (&lv)[kNQ]) {
-  const float4* lp = reinterpret_cast<const float4*>(lg + i * kNQ);
-  const float4 x0 = lp[0], x1 = lp[1];
+  const float4* lp = reinterpret_cast<const float4*>(lg + (i >> 6) * (64 * kNQ)) + (i & 63);
+  const float4 x0 = lp[0], x1 = lp[64];
   lv[0] = x0.x; lv[1] = x0.y; lv[2] = x0.z; lv[3] = x0.w;
   lv[4] = x1.x; lv[5] = x1.y; lv[6] = x1.z; lv[7] = x1.w;
 }
@@ -209,7 +212,7 @@ struct DemandArgs {
   const int32_t* req_order;
   int32_t* row_counter;
   const float* qhat;
-  float* ring_logits;   // [blocks][ring_tokens][8]
+  float* ring_logits;   // [blocks][ring_tokens / 64][2][64][4]
   float* ring_keys;     // [blocks][ring_tokens][2]
   int64_t ring_tokens;
   float* imp;
@@ -343,10 +346,9 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
           wave_order();
         }
         if (cur_bad && lane == 0) atomicOr(a.err, GP_DEVERR_PAGE);
-        const int64_t tok = (int64_t)tcur * 64 + lane;
-        float4* out = reinterpret_cast<float4*>(lg + tok * kNQ);
+        float4* out = reinterpret_cast<float4*>(lg + (int64_t)tcur * (64 * kNQ)) + lane;
         out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        out[64] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         if ((tcur >> 2) < P - 1) {
 #pragma unroll
           for (int q = 0; q < kNQ; ++q) md[q] = fmaxf(md[q], acc[q]);
