@@ -103,9 +103,10 @@ typedef struct gp_config {
                             must be <= tau; used by GP_POLICY_SHRINK only */
   int32_t min_tokens;    /* capacity floor: Shrink only if (P - 1) b >= min_tokens
                             [1024] (App. H.1) */
-  int32_t compact_workgroups; /* workgroups (512 threads) of the compaction kernel; 0 = 4 per
-                                 CU.  A smaller count leaves CUs to work on other streams,
-                                 e.g. decoding beside asynchronous compression (App. E.3) */
+  int32_t compact_workgroups; /* workgroups (1024 threads) of the compaction kernel; 0 = 2
+                                 per CU.  A smaller count leaves CUs to work on other
+                                 streams, e.g. decoding beside asynchronous compression
+                                 (App. E.3) */
 } gp_config;
 
 /* Global page pool (§4.2): K/V storage and the device free-page stack. */

@@ -178,7 +178,7 @@ class Config:
     policy: int = GP_POLICY_GROWPAGE
     shrink_tau: float = -0.005
     min_tokens: int = 1024
-    compact_workgroups: int = 0  # 0: 4 per CU
+    compact_workgroups: int = 0  # 0: 2 per CU
 
     @property
     def max_freed(self) -> int:

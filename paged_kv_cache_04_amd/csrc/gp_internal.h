@@ -27,7 +27,7 @@ constexpr int64_t kMaxRequestTokens = int64_t(1) << 23;
 constexpr int kDemandBlocksPerCU = GP_DEMAND_BLOCKS_PER_CU;
 // Compaction: persistent workgroups per CU when the context sets no count.
 #ifndef GP_COMPACT_BLOCKS_PER_CU
-#define GP_COMPACT_BLOCKS_PER_CU 4
+#define GP_COMPACT_BLOCKS_PER_CU 2
 #endif
 // Decode attention: persistent workgroups per CU of the unit kernel.
 #ifndef GP_DECODE_BLOCKS_PER_CU

@@ -9,9 +9,10 @@
 // a Shrink row of the GrowPage-Shrink policy, App. H.1) (one search
 // per destination row, kept with both addresses in a per-chunk table).
 // Slots before the first dropped one stay where they are.  Each source lies
-// at most 2b slots after its destination, so the workgroup walks destinations
-// in 512-row chunks (128 KiB, 16 pieces of 16 bytes per thread): it loads a
-// whole chunk into registers, waits for the loads and barriers, then stores.
+// at most 2b slots after its destination, so the workgroup (1024 threads)
+// walks destinations in 1024-row chunks (256 KiB, 16 pieces of 16 bytes per
+// thread): it loads a whole chunk into registers, waits for the loads and
+// barriers, then stores.
 // Loads and stores are non-temporal: each byte is touched once, and keeping
 // it out of the caches leaves them to the next event's demand pass.  A
 // chunk's stores land below every later chunk's sources, and every earlier
@@ -31,9 +32,9 @@ namespace gp {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCT = 512;                      // threads
+constexpr int kCT = 1024;                     // threads
 constexpr int kPer = 16;                      // 16-byte pieces per thread per chunk
-constexpr int kRowsC = kCT * kPer / 16;       // destination rows per chunk (512)
+constexpr int kRowsC = kCT * kPer / 16;       // destination rows per chunk (1024)
 constexpr int kMaxPages = 65536 / kPage;      // pages per row held in LDS
 
 __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stride,
