@@ -36,6 +36,7 @@ constexpr int kCT = 1024;                     // threads
 constexpr int kPer = 16;                      // 16-byte pieces per thread per chunk
 constexpr int kRowsC = kCT * kPer / 16;       // destination rows per chunk (1024)
 constexpr int kMaxPages = 65536 / kPage;      // pages per row held in LDS
+static_assert(kRowsC <= kCT, "one chunk-table row per thread");
 
 __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stride,
                                                  int pool_pages,
