@@ -11,8 +11,9 @@
 // bottom, on the row held in LDS when it fits (read from HBM once):
 //   1. the b smallest candidates of C: a 3-digit radix select (11 + 10 + 10
 //      bits) finds the value v of the b-th smallest; candidates below v are
-//      dropped and of those equal to v the oldest until exactly b (block-wide
-//      prefix count in slot order); dropped slots written in ascending order;
+//      dropped and of those equal to v the oldest until exactly b (ranks in
+//      slot order from ballots over per-wave slot ranges); dropped slots
+//      written in ascending order;
 //   2. if no block loses more than |B_j| - min(k_loc, |B_j|) candidates, no
 //      protected (block top-k_loc) candidate was dropped and this is Eq. 10's
 //      answer; otherwise each block's top-min(k_loc, |B_j|) is marked (one
@@ -29,33 +30,6 @@ constexpr int kMaxRowTokens = 65536;
 constexpr int kSelLdsTokens = 32768;  // candidates held in LDS (128 KiB)
 constexpr int kSelH1 = 2048;          // first radix digit: bits 30..20
 constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
-
-// Exclusive prefix sum over the block (1024 threads); total in *total.
-__device__ __forceinline__ int block_excl_scan(int v, int* buf, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) buf[wv] = x;
-  __syncthreads();
-  if (wv == 0) {
-    int w = lane < kSel / 64 ? buf[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kSel / 64; off <<= 1) {
-      const int y = __shfl_up(w, off);
-      if (lane >= off) w += y;
-    }
-    if (lane < kSel / 64) buf[lane] = w;
-  }
-  __syncthreads();
-  const int base = wv > 0 ? buf[wv - 1] : 0;
-  *total = buf[kSel / 64 - 1];
-  __syncthreads();
-  return base + x - v;
-}
 
 // Steps 2-3: the nd smallest candidates of [0, nc) (skipping those marked in
 // the S_loc bitmap when PROT), written ascending to dst (and dst2); without
@@ -121,44 +95,70 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
   const uint32_t v = prefix;
   const int need = nd - (int)below;
 
-  // step 3: ties at v go oldest first; write dropped slots in ascending order
-  const int q = (nc + kSel - 1) / kSel;
-  const int lo = t * q < nc ? t * q : nc;
-  const int hi = lo + q < nc ? lo + q : nc;
-  int ties = 0;
-  for (int i = lo; i < hi; ++i)
-    if (!(PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) && __float_as_uint(s[i]) == v) ++ties;
-  int total;
-  const int tie0 = block_excl_scan(ties, scanbuf, &total);
-  int mine = 0;  // this thread's drops
+  // step 3: ties at v go oldest first; dropped slots are written in
+  // ascending order.  Each wave walks one contiguous range of slots, 64 at a
+  // time (one per lane, so the row is read in whole 256-byte lines); ranks in
+  // slot order come from ballots within a wave and, across waves, from the
+  // counts of the waves before it.
+  constexpr int kW = kSel / 64;
+  const int span = (nc + kW * 64 - 1) / (kW * 64) * 64;  // slots per wave
+  const int w0 = wv * span;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
+  auto cand = [&](int i, uint32_t& key) -> bool {
+    if (i >= nc || (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u))) return false;
+    key = __float_as_uint(s[i]);
+    return true;
+  };
   {
-    int tr = tie0;
-    for (int i = lo; i < hi; ++i) {
-      if (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) continue;
-      const uint32_t key = __float_as_uint(s[i]);
-      if (key < v) ++mine;
-      else if (key == v) mine += (tr++ < need);
+    int nt = 0, nl = 0;
+    for (int j = 0; j < span; j += 64) {
+      uint32_t key = 0;
+      const bool ok = cand(w0 + j + lane, key);
+      nt += __popcll(__ballot(ok && key == v));
+      nl += __popcll(__ballot(ok && key < v));
+    }
+    if (lane == 0) {
+      scanbuf[wv] = nt;
+      scanbuf[kW + wv] = nl;
     }
   }
-  const int pos0 = block_excl_scan(mine, scanbuf, &total);
-  {
-    int tr = tie0, pos = pos0;
-    for (int i = lo; i < hi; ++i) {
-      if (PROT && ((sloc[i >> 5] >> (i & 31)) & 1u)) continue;
-      const uint32_t key = __float_as_uint(s[i]);
-      bool drop = key < v;
-      if (key == v) drop = tr++ < need;
-      if (drop) {
-        if (pos < nd) {
-          dst[pos] = i;
-          if (dst2) dst2[pos] = i;
-          if (!PROT) atomicAdd(&blkcnt[i >> 8], 1);
-        }
-        ++pos;
-      }
+  __syncthreads();
+  // ties and drops of the waves before this one; the row's total drops
+  int tr = 0, pos = 0, tb = 0, db = 0;
+  for (int u = 0; u < kW; ++u) {
+    if (u == wv) {
+      tr = tb;
+      pos = db;
     }
+    const int tu = scanbuf[u];
+    int take = need - tb;
+    take = take < 0 ? 0 : (take > tu ? tu : take);
+    db += scanbuf[kW + u] + take;
+    tb += tu;
   }
-  return total;
+  for (int j = 0; j < span; j += 64) {
+    const int i = w0 + j + lane;
+    uint32_t key = 0;
+    const bool ok = cand(i, key);
+    const bool tie = ok && key == v;
+    const uint64_t tm = __ballot(tie);
+    const bool drop = (ok && key < v) || (tie && tr + __popcll(tm & lt) < need);
+    const uint64_t dm = __ballot(drop);
+    const int p = pos + __popcll(dm & lt);
+    if (drop && p < nd) {
+      dst[p] = i;
+      if (dst2) dst2[p] = i;
+    }
+    // a 64-slot step lies in one page: one count per step and wave
+    if (!PROT && lane == 0 && dm != 0) {
+      const int room = nd - pos;  // drops of this step that are written
+      const int cnt = __popcll(dm);
+      if (room > 0) atomicAdd(&blkcnt[(w0 + j) >> 8], cnt < room ? cnt : room);
+    }
+    tr += __popcll(tm);
+    pos += __popcll(dm);
+  }
+  return db;
 }
 
 // Step 1: S_loc of every block as a bitmap.
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   __shared__ __attribute__((aligned(16))) float srow[kSelLdsTokens];
   __shared__ uint32_t sloc[kMaxRowTokens / 32];
   __shared__ uint32_t hcnt[kSelH1];
-  __shared__ int scanbuf[kSel / 64];
+  __shared__ int scanbuf[2 * (kSel / 64)];
   __shared__ int blkcnt[kMaxRowTokens / kPage];
   __shared__ uint32_t s_prefix, s_below;
   if (!hdr->valid) return;
