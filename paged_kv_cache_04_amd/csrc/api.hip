@@ -262,11 +262,15 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   }
   const gp::WsLayout w = gp::ws_layout(p, c->batch, c->total_tokens, c->max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = timed(c, GP_K_SHARE, s, [&] {
-    return gp::launch_share(p, w, c->batch, action, pool->num_pages, bt->block_table,
-                            bt->max_pages, pool->refcount, pool->free_stack, pool->free_count, ws,
-                            c->d_counters, c->d_err, s);
-  });
+  // the request flags start cleared (gp_demand's plan); only prefix sharing
+  // needs the target-page step
+  hipError_t e = hipSuccess;
+  if (shared)
+    e = timed(c, GP_K_SHARE, s, [&] {
+      return gp::launch_share(p, w, c->batch, action, pool->num_pages, bt->block_table,
+                              bt->max_pages, pool->refcount, pool->free_stack, pool->free_count,
+                              ws, c->d_counters, c->d_err, s);
+    });
   if (e == hipSuccess)
     e = timed(c, GP_K_SELECT, s, [&] {
       return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);

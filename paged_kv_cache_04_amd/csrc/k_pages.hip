@@ -58,8 +58,9 @@ __device__ __forceinline__ int load_agent(const int32_t* p) {
 // later one that needs a page, as in a serial walk that stops allocating at
 // the first failure.  target[page_off[r] + i] = new page or -1;
 // req_flags[r] = kReqBlocked for a request left uncompressed.
-// counters[4] counts the pages allocated.  Without reference counts the
-// kernel only clears req_flags.
+// counters[4] counts the pages allocated.  Launched only with reference
+// counts (the batch plan clears req_flags); on a rejected batch it clears
+// req_flags and returns.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMaxBatch) void k_share(int B, int b, int stride, int pool_pages,
                                                      const WsHeader* __restrict__ hdr,

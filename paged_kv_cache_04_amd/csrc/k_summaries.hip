@@ -67,7 +67,8 @@ hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int3
 // ---------------------------------------------------------------------------
 // Batch plan: prefix sums of the device page counts (page_off[r] = sum of P
 // over requests before r), the demand kernel's work order (requests by page
-// count, largest first, ties by index) and its queue counter.  The batch is
+// count, largest first, ties by index) and its queue counter, and clears the
+// per-request flags of the compression that follows.  The batch is
 // accepted (header.valid = 1) only if every count lies in [1, max_pages], no
 // request is longer than the workspace's per-row rings and the total equals
 // the host's; every later kernel of the event exits at once on a rejected
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
                                                int64_t ring_tokens, WsHeader* __restrict__ hdr,
                                                int64_t* __restrict__ page_off,
                                                int32_t* __restrict__ req_order,
+                                               int32_t* __restrict__ req_flags,
                                                int32_t* __restrict__ err) {
   __shared__ int64_t buf[kMaxBatch];
   __shared__ int32_t pages[kMaxBatch];
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
     __syncthreads();
   }
   if (t < B) {
+    req_flags[t] = 0;
     page_off[t + 1] = buf[t];
     const int32_t mine = pages[t];
     int rank = 0;
@@ -128,7 +131,8 @@ hipError_t launch_plan(const Params& p, const WsLayout& w, const int32_t* num_pa
                      host_total_pages, p.b, w.ring_tokens,
                      reinterpret_cast<WsHeader*>(base + w.header),
                      reinterpret_cast<int64_t*>(base + w.page_off),
-                     reinterpret_cast<int32_t*>(base + w.req_order), err);
+                     reinterpret_cast<int32_t*>(base + w.req_order),
+                     reinterpret_cast<int32_t*>(base + w.req_flags), err);
   return hipGetLastError();
 }
 
