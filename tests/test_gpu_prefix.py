@@ -15,8 +15,10 @@ import torch
 
 import oracle
 from paged_kv_cache_04_amd import synth
-from gpu_util import HostCopy, check_decode_after_event, gb_config, log
-from test_gpu_tiny import check_event
+from paged_kv_cache_04_amd import binding as gb
+from gpu_util import (HostCopy, check_decode_after_event, device_rows, gb_config, log,
+                      oracle_config, oracle_event, run_stream_gpu, run_stream_oracle, runner_for)
+from test_gpu_tiny import ERR_NOPAGE, check_event
 
 pytestmark = pytest.mark.gpu
 
@@ -118,3 +120,59 @@ def test_prefix_sharing_shrink_shared_last_page():
     assert ref["ok"].all()
     assert ref["copied"] == 14 and ref["shrunk"] == 3
     assert ref["refcount"][bt0[2, 4]] == 1
+
+
+@needs_gpu
+def test_blocked_requests_compress_in_the_next_plain_event():
+    """Request flags live in the workspace: an event with reference counts
+    that leaves requests 3-6 uncompressed for want of target pages (as in the
+    page-shortage test) must not leave them blocked in the next event on the
+    same context and workspace.  The K/V pages, block tables and free stack
+    are restored to the layout before any sharing, the pool is passed
+    without reference counts, and every request's dropped slots and
+    compacted bytes are compared with the oracle's plain event."""
+    log("test_blocked_requests_compress_in_the_next_plain_event")
+    P = [6, 6, 5, 7, 4, 6, 3, 5]
+    wl = synth.make_workload(SMALL, P, 64, seed=5151, device="cuda", align=["S"] * 8,
+                             cluster_sizes=[30] * 8, free_pages=0, steps=120, short_steps=16,
+                             max_slots=8)
+    plain = [(x, x.clone()) for x in (wl.k_pool, wl.v_pool, wl.block_table, wl.num_pages,
+                                      wl.num_tokens, wl.free_stack, wl.free_count)]
+    rc = share_prefixes(wl, [(1, 0, 3), (2, 0, 2), (4, 3, 4), (6, 5, 1)])
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    ocfg = oracle_config(cfg)
+    run = runner_for(wl, cfg, refcount=rc)
+    q = run_stream_gpu(run, wl)
+    zeros = torch.zeros(len(P), dtype=torch.int8, device="cuda")
+    run.demand(q)
+    run.action.copy_(zeros)
+    run.compress()
+    torch.cuda.synchronize()
+    assert run.device_errors() == ERR_NOPAGE  # requests 3-6 were left uncompressed
+
+    for dst, src in plain:
+        dst.copy_(src)
+    run.pool = gb.Pool(wl.k_pool, wl.v_pool, wl.free_stack, wl.free_count)
+    run.dropped.fill_(-1)
+    hc = HostCopy(wl)
+    state_o, q_o = run_stream_oracle(wl, ocfg)
+    run.demand(q)
+    run.action.copy_(zeros)
+    run.compress()
+    torch.cuda.synchronize()
+    assert run.device_errors() == 0
+    ref = oracle_event(ocfg, hc, state_o, q_o, action=np.zeros(len(P), np.int8))
+    dropped = run.dropped.cpu().numpy()
+    nt = run.batch.num_tokens.cpu().numpy()
+    for r in range(len(P)):
+        assert ref["freed"][r] == 1
+        N = P[r] * ocfg.b
+        assert nt[r] == N - ocfg.b, r
+        pages = hc.bt[r, :P[r]]
+        for l in range(ocfg.L):
+            for h in range(ocfg.Hkv):
+                assert np.array_equal(dropped[r, l, h, :ocfg.b], ref["dropped"][(r, l, h)]), (r, l, h)
+                kw, vw = ref["compacted"][(r, l, h)]
+                assert np.array_equal(device_rows(wl.k_pool, l, h, pages)[:N - ocfg.b], kw), (r, l, h)
+                assert np.array_equal(device_rows(wl.v_pool, l, h, pages)[:N - ocfg.b], vw), (r, l, h)
+    log("  every request compressed in the plain event")
