@@ -44,7 +44,9 @@
  *    frequencies f_j, then sin(p * f_j) (rotate-half pairing (j, j + d/2)).
  *
  * Version 1 limits: d = 128, b = 256, Hq / Hkv = 4, batch <= 1024, at most
- * 2^23 cached tokens (32768 pages) per request.
+ * 2^23 cached tokens (32768 pages) per request for gp_demand and
+ * gp_grow_page, at most 65536 tokens (256 pages) per compressed request
+ * (a longer one is skipped with GP_DEVERR_LONG).
  */
 #ifndef GROWPAGE_H
 #define GROWPAGE_H
@@ -71,8 +73,11 @@ enum gp_err_bits {
   GP_DEVERR_PAGE = 4,      /* page id outside [0, num_pages): tile skipped */
   GP_DEVERR_SHORT = 8,     /* compress requested with fewer than 2 pages */
   GP_DEVERR_PAGES = 16,    /* device page count outside [1, max_pages] */
-  GP_DEVERR_NOPAGE = 32    /* no free pages to replace a compressing request's
+  GP_DEVERR_NOPAGE = 32,   /* no free pages to replace a compressing request's
                               shared pages (App. E.2): request left uncompressed */
+  GP_DEVERR_LONG = 64      /* compress asked of a request longer than 65536 tokens
+                              (the version 1 selection limit): request left as it
+                              was, the rest of the batch is compressed */
 };
 
 /* Actions and decisions (int8 on the device). */
@@ -141,8 +146,8 @@ typedef struct gp_demand_out {
   int64_t* k_diff;   /* [B] sum K^S - sum K^L (may be NULL) */
   double* delta;     /* [B] Delta_t = r^S - r^L (Eq. 8) (may be NULL) */
   int8_t* decision;  /* [B] GP_GROW iff Delta_t > tau, else GP_COMPRESS; with
-                        GP_POLICY_SHRINK, GP_SHRINK iff Delta_t < shrink_tau and
-                        (P - 1) b >= min_tokens */
+                        GP_POLICY_SHRINK, GP_SHRINK iff Delta_t < shrink_tau,
+                        P >= 3 and (P - 1) b >= min_tokens */
   float* abar;       /* optional [sum over rows of N][2]: the full-cache attention
                         distributions (short, long) per token, rows in (request,
                         layer, KV head) order; NULL skips the write */
@@ -224,7 +229,9 @@ gp_status gp_grow_page(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
  * page is pushed on the free stack (requests in index order), its block-table
  * entry set to -1, P -= 1 and num_tokens = (P-2) b with the old P; a Shrink
  * with fewer than 3 pages sets GP_DEVERR_SHORT and leaves the request as it
- * was; under GP_POLICY_GROWPAGE a GP_SHRINK action is ignored.
+ * was; under GP_POLICY_GROWPAGE a GP_SHRINK action is ignored.  A request
+ * longer than 65536 tokens is left as it was (GP_DEVERR_LONG) while the rest
+ * of the batch is compressed.
  * Prefix sharing (App. E.2; pool->refcount != NULL): a page with more than
  * one reference is never written.  Before selection, each compressing
  * request gets a new target page for every shared page it keeps (its P

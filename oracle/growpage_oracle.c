@@ -315,7 +315,11 @@ int orc_decide(const int32_t* ks, const int32_t* kl, int n_rows,
  *   shrink_tau <= Delta <= tau     -> Compress & Hold
  *   Delta < shrink_tau             -> Shrink, unless the capacity left after
  *                                     it, (P - 1) b, would fall below
- *                                     min_tokens (then Compress & Hold).
+ *                                     min_tokens, or the request holds fewer
+ *                                     than 3 pages (then Compress & Hold):
+ *                                     Shrink keeps (P - 2) b slots including
+ *                                     the recent window, so Eq. 10's budget
+ *                                     (P - 2) b - R is negative below 3.
  * Shrink drops two pages worth of slots and returns one page to the pool
  * (orc_select_pages with 2 pages, orc_return_pages).  A request of one page
  * grows, as in orc_decide.
@@ -330,7 +334,8 @@ int orc_decide_shrink(const int32_t* ks, const int32_t* kl, int n_rows,
   const int base = orc_decide(ks, kl, n_rows, card_c, tau, diff_out, &delta);
   if (delta_out) *delta_out = delta;
   if (base == ORC_GROW) return ORC_GROW;
-  if (delta < shrink_tau && (int64_t)(num_pages - 1) * b >= min_tokens) return ORC_SHRINK;
+  if (delta < shrink_tau && num_pages >= 3 && (int64_t)(num_pages - 1) * b >= min_tokens)
+    return ORC_SHRINK;
   return ORC_COMPRESS;
 }
 

@@ -250,11 +250,11 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
     return GP_ERR_INVALID_ARG;
   // Eq. 10 needs the local quotas to fit the budget K_t = (P - m) b - R,
   // m = 1 for Compress & Hold, 2 for Shrink (any request with 3 or more pages
-  // may shrink under GP_POLICY_SHRINK).
+  // may shrink under GP_POLICY_SHRINK).  Requests too short or too long to
+  // compress are flagged on the device if they are asked to, and skipped.
   for (int r = 0; r < c->batch; ++r) {
     const int64_t P = c->pages[r];
-    if (P < 2) continue;  // flagged on the device if it is asked to compress
-    if (P * p.b > 65536) return GP_ERR_UNSUPPORTED;
+    if (P < 2 || P * p.b > gp::kMaxCompressTokens) continue;
     const int64_t kq = p.kloc;
     const int64_t loc = (P - 1) * (kq < p.b ? kq : p.b) + (kq < p.b - p.R ? kq : p.b - p.R);
     const int64_t m = (p.policy == GP_POLICY_SHRINK && P >= 3) ? 2 : 1;

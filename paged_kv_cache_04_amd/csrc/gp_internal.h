@@ -66,6 +66,10 @@ struct WsHeader {
 // Per-request state of one gp_compress_hold call (req_flags).
 constexpr int32_t kReqBlocked = 1;    // shared pages could not be replaced: not compressed
 constexpr int32_t kReqCompacted = 2;  // K/V compacted (set by the compaction kernel)
+constexpr int32_t kReqTooLong = 4;    // longer than the selection takes: not compressed
+// Longest request the selection and compaction kernels take (their per-row
+// page lists and block counts live in LDS).
+constexpr int64_t kMaxCompressTokens = 65536;
 
 // Workspace: batch plan, calibrated summaries, per-token importance (read by
 // gp_compress_hold), dropped slots, per-request flags and target pages of the

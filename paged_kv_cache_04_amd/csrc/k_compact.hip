@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
     const int nd = m * b;                    // dropped slots
     const int P = __builtin_amdgcn_readfirstlane((int)(page_off[r + 1] - page_off[r]));
     if (P < m + 1) return;
-    if (__builtin_amdgcn_readfirstlane(req_flags[r]) & kReqBlocked) return;  // pages short
+    // pages short (App. E.2), or longer than the selection takes
+    if (__builtin_amdgcn_readfirstlane(req_flags[r]) & (kReqBlocked | kReqTooLong)) return;
     const int l = lh / Hkv, h = lh % Hkv;
     if (t == 0) {
       bad = 0;

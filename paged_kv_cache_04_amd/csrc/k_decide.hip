@@ -49,8 +49,11 @@ __global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau, int p
     if (delta) delta[r] = dl;
     int8_t dec = grow ? GP_GROW : GP_COMPRESS;
     // GrowPage-Shrink (App. H.1 Eq. 13): below shrink_tau, and only while
-    // (P - 1) b tokens of capacity, at least min_tokens, would remain
-    if (policy == GP_POLICY_SHRINK && !grow && dl < shrink_tau && (P - 1) * b >= min_tokens)
+    // (P - 1) b tokens of capacity, at least min_tokens, would remain; a
+    // Shrink drops two pages of slots and keeps the recent window, so Eq. 10's
+    // budget (P - 2) b - R needs P >= 3 (a shorter request compresses)
+    if (policy == GP_POLICY_SHRINK && !grow && dl < shrink_tau && P >= 3 &&
+        (P - 1) * b >= min_tokens)
       dec = GP_SHRINK;
     decision[r] = dec;
   }

@@ -31,8 +31,10 @@ __device__ void block_scan(int* v) {
 // that does not compress.  Mirrors the action checks of the select and
 // compaction kernels (a Shrink counts only when the dropped-slot stride has
 // room for 2b slots, i.e. under the GrowPage-Shrink policy).
-__device__ int kept_pages(const int8_t* action, int r, int64_t P, int b, int stride) {
+__device__ int kept_pages(const int8_t* action, int r, int64_t P, int b, int stride,
+                          int32_t flags) {
   const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+  if (flags & kReqTooLong) return 0;  // the selection skips it
   int m = 0;
   if (act == GP_COMPRESS) m = 1;
   if (act == GP_SHRINK && stride >= 2 * b) m = 2;
@@ -57,7 +59,9 @@ __device__ __forceinline__ int load_agent(const int32_t* p) {
 // Since S_r only grows, the first request that cannot be served blocks every
 // later one that needs a page, as in a serial walk that stops allocating at
 // the first failure.  target[page_off[r] + i] = new page or -1;
-// req_flags[r] = kReqBlocked for a request left uncompressed.
+// req_flags[r] = kReqBlocked for a request left uncompressed.  A request the
+// batch plan flagged kReqTooLong is not compressed: it needs no target and
+// keeps its flag.
 // counters[4] counts the pages allocated.  Launched only with reference
 // counts (the batch plan clears req_flags); on a rejected batch it clears
 // req_flags and returns.
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(kMaxBatch) void k_share(int B, int b, int stride, i
   __syncthreads();
   for (int r = wv; r < B; r += kWaves) {
     const int64_t P = page_off[r + 1] - page_off[r];
-    const int keep = kept_pages(action, r, P, b, stride);
+    const int keep = kept_pages(action, r, P, b, stride, req_flags[r]);
     const int32_t* bt = block_table + (int64_t)r * max_pages;
     int cnt = 0;
     for (int i0 = 0; i0 < keep; i0 += 64) {
@@ -111,12 +115,13 @@ __global__ __launch_bounds__(kMaxBatch) void k_share(int B, int b, int stride, i
     const int incl = cum[r];
     const int own = incl - (r > 0 ? cum[r - 1] : 0);
     const bool served = own == 0 || incl <= fc;
+    const int32_t flags = __builtin_amdgcn_readfirstlane(req_flags[r]);
     if (lane == 0) {
-      req_flags[r] = served ? 0 : kReqBlocked;
+      req_flags[r] = (flags & kReqTooLong) | (served ? 0 : kReqBlocked);
       if (!served) s_blocked = 1;
     }
     const int64_t P = page_off[r + 1] - page_off[r];
-    const int keep = served ? kept_pages(action, r, P, b, stride) : 0;
+    const int keep = served ? kept_pages(action, r, P, b, stride, flags) : 0;
     const int32_t* bt = block_table + (int64_t)r * max_pages;
     int32_t* tg = target + page_off[r];
     int taken = incl - own;

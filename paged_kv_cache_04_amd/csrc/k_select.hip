@@ -279,6 +279,10 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
   const int64_t P = page_off[r + 1] - page_off[r];
   const int t = threadIdx.x;
+  if (req_flags[r] & kReqTooLong) {  // longer than the selection takes: left as it is
+    if (t == 0 && lh == 0) atomicOr(err, GP_DEVERR_LONG);
+    return;
+  }
   if (P < m + 1) {
     if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
     return;

@@ -67,8 +67,9 @@ hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int3
 // ---------------------------------------------------------------------------
 // Batch plan: prefix sums of the device page counts (page_off[r] = sum of P
 // over requests before r), the demand kernel's work order (requests by page
-// count, largest first, ties by index) and its queue counter, and clears the
-// per-request flags of the compression that follows.  The batch is
+// count, largest first, ties by index) and its queue counter, and resets the
+// per-request flags of the compression that follows (a request longer than
+// the compression takes is flagged kReqTooLong).  The batch is
 // accepted (header.valid = 1) only if every count lies in [1, max_pages], no
 // request is longer than the workspace's per-row rings and the total equals
 // the host's; every later kernel of the event exits at once on a rejected
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
     __syncthreads();
   }
   if (t < B) {
-    req_flags[t] = 0;
+    req_flags[t] = (int64_t)pages[t] * b > kMaxCompressTokens ? kReqTooLong : 0;
     page_off[t + 1] = buf[t];
     const int32_t mine = pages[t];
     int rank = 0;

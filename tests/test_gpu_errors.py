@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU in this container")
 
 SMALL = synth.ModelShape("small", L=2, Hq=8, Hkv=2, theta=1e4)
-ERR_SLOT, ERR_POSITION, ERR_PAGE, ERR_SHORT, ERR_PAGES = 1, 2, 4, 8, 16
+ERR_SLOT, ERR_POSITION, ERR_PAGE, ERR_SHORT, ERR_PAGES, ERR_LONG = 1, 2, 4, 8, 16, 64
+ONE_HEAD = synth.ModelShape("one-head", L=1, Hq=4, Hkv=1, theta=1e4)
 
 
 def _workload(seed):
@@ -175,3 +176,57 @@ def test_compaction_grid_sizes_give_identical_bytes(groups):
         del run, wl
     for a, b in zip(results[0], results[1]):
         assert torch.equal(a, b)
+
+
+@needs_gpu
+def test_compress_skips_request_beyond_selection_limit():
+    """A request longer than the 65536 tokens the selection takes, whose
+    decision is Compress & Hold in an event where the grant step has already
+    given another request a page, is left as it was (LONG bit, same bytes
+    and token count), while the rest of the batch is compressed or grown as
+    the oracle says: nothing is refused half-way through an event."""
+    from gpu_util import HostCopy, oracle_config, oracle_event, run_stream_oracle
+    log("test_compress_skips_request_beyond_selection_limit")
+    P = [257, 5, 3]
+    wl = synth.make_workload(ONE_HEAD, P, 268, seed=4250, device="cuda", align=["S", "S", "L"],
+                             cluster_sizes=[30, 30, 30], free_pages=1, steps=60, short_steps=8,
+                             max_slots=4)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    hc = HostCopy(wl)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    k0 = device_rows(wl.k_pool, 0, 0, hc.bt[0, :P[0]])
+    v0 = device_rows(wl.v_pool, 0, 0, hc.bt[0, :P[0]])
+    run.demand(q)
+    run.grow()
+    run.compress()
+    torch.cuda.synchronize()
+    assert run.device_errors() == ERR_LONG
+    ocfg = oracle_config(cfg)
+    state, qcur = run_stream_oracle(wl, ocfg)
+    ref = oracle_event(ocfg, hc, state, qcur)
+    action = run.action.cpu().numpy()
+    log(f"  actions {action.tolist()}")
+    np.testing.assert_array_equal(action, ref["action"])
+    assert action[0] == 0  # the long request was to compress
+    np.testing.assert_array_equal(run.out.k_short.cpu().numpy(), ref["dem"]["ks"])
+    np.testing.assert_array_equal(run.out.k_long.cpu().numpy(), ref["dem"]["kl"])
+    np.testing.assert_array_equal(wl.block_table.cpu().numpy(), ref["bt"])
+    np.testing.assert_array_equal(wl.num_pages.cpu().numpy(), ref["P"])
+    nt = wl.num_tokens.cpu().numpy()
+    assert nt[0] == P[0] * 256
+    assert np.array_equal(device_rows(wl.k_pool, 0, 0, hc.bt[0, :P[0]]), k0)
+    assert np.array_equal(device_rows(wl.v_pool, 0, 0, hc.bt[0, :P[0]]), v0)
+    dropped = run.dropped.cpu().numpy()
+    assert np.all(dropped[0] == -1)
+    for r in (1, 2):
+        if action[r] != 0:
+            assert nt[r] == P[r] * 256 and np.all(dropped[r] == -1)
+            continue
+        np.testing.assert_array_equal(dropped[r, 0, 0, :256], ref["dropped"][(r, 0, 0)])
+        k_want, v_want = ref["compacted"][(r, 0, 0)]
+        n = k_want.shape[0]
+        assert nt[r] == n
+        pages = hc.bt[r, :hc.P[r]]
+        assert np.array_equal(device_rows(wl.k_pool, 0, 0, pages)[:n], k_want)
+        assert np.array_equal(device_rows(wl.v_pool, 0, 0, pages)[:n], v_want)

@@ -182,6 +182,31 @@ def test_shrink_policy_batch():
 
 
 @needs_gpu
+def test_shrink_needs_three_pages():
+    """GrowPage-Shrink with no capacity floor (min_tokens = 0): a Shrink keeps
+    (P - 2) b slots including the recent window, so Eq. 10's budget needs
+    P >= 3 (App. H.1 Eq. 13; §3.3 Eq. 10).  Short-view requests of 2, 3 and 5
+    pages: the 2-page one compresses instead of shrinking (no SHORT error,
+    compacted as the oracle says), the others shrink; every output against
+    the oracle."""
+    log("test_shrink_needs_three_pages")
+    P = [2, 3, 5, 2]
+    wl = synth.make_workload(SMALL, P, 20, seed=4246, device="cuda", align=["S"] * len(P),
+                             cluster_sizes=[30] * len(P), free_pages=0, steps=120,
+                             short_steps=16, max_slots=8)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots, policy=1, min_tokens=0)
+    ref = check_event(wl, cfg, check_f64=False)
+    act = list(ref["action"])
+    delta = ref["dem"]["delta"]
+    log(f"  actions {act}, delta {[round(float(x), 4) for x in delta]}")
+    two = [r for r in range(len(P)) if P[r] == 2 and delta[r] < cfg.shrink_tau]
+    assert two, "no 2-page request below the Shrink threshold"
+    assert all(act[r] == 0 for r in two)
+    assert all(act[r] == 2 for r in range(len(P)) if P[r] >= 3 and delta[r] < cfg.shrink_tau)
+    assert 2 in act
+
+
+@needs_gpu
 def test_shrink_ignored_under_default_policy():
     """A caller-forced GP_SHRINK action under the default policy changes
     nothing (the workspace holds one page of drops per row)."""

@@ -349,7 +349,8 @@ def test_decide_sign_and_eq8_mean():
 def test_decide_shrink_three_regions():
     """orc_decide_shrink (Appendix H.1 Eq. 13): Shrink below -0.005, Compress
     & Hold on [-0.005, 0] (both ends included), Grow above 0; Shrink only
-    when (P - 1) b >= 1024 tokens remain; a one-page request grows."""
+    when (P - 1) b >= 1024 tokens remain and the request holds at least 3
+    pages; a one-page request grows."""
     cfg = OracleConfig(L=1, Hq=4, Hkv=1, b=200, policy=1, min_tokens=1000)
     one = np.array([0], np.int32)
     # P = 6, b = 200: |C_t| = 1000, Delta = diff / 1000 with one row
@@ -364,6 +365,11 @@ def test_decide_shrink_three_regions():
     assert oracle.decide(cfg, one, np.array([900], np.int32), 4 * 256, 5)[0] == oracle.SHRINK
     assert oracle.decide(cfg, one, np.array([900], np.int32), 3 * 256, 4)[0] == oracle.COMPRESS
     assert oracle.decide(cfg, one, np.array([9], np.int32), 0, 1)[0] == oracle.GROW
+    # a Shrink keeps (P - 2) b slots with the recent window: with no capacity
+    # floor a 3-page request shrinks, a 2-page one compresses
+    cfg = OracleConfig(L=1, Hq=4, Hkv=1, b=256, policy=1, min_tokens=0)
+    assert oracle.decide(cfg, one, np.array([900], np.int32), 2 * 256, 3)[0] == oracle.SHRINK
+    assert oracle.decide(cfg, one, np.array([900], np.int32), 1 * 256, 2)[0] == oracle.COMPRESS
     # the default policy never shrinks
     cfg = OracleConfig(L=1, Hq=4, Hkv=1, b=256)
     assert oracle.decide(cfg, one, np.array([900], np.int32), 4 * 256, 5)[0] == oracle.COMPRESS
