@@ -28,9 +28,11 @@ def _threads() -> int:
 class OracleEvents:
     def __init__(self, ocfg: oracle.OracleConfig, wl, rows=None):
         """rows: (r, l, h) tracked rows; None tracks every row.  Requests
-        with a tracked row keep their summary state; the decision and the
-        page grant need every row of a request, so with a subset they are
-        taken from `decision_override` at event time."""
+        with a tracked row keep their summary state.  The decision of a
+        request needs all of its rows: it is computed for every request
+        whose rows are all tracked (`full_reqs`); with a subset of the
+        requests the page grant takes its decisions from
+        `decision_override` at event time."""
         self.cfg = ocfg
         s = wl.shape
         self.B = wl.B
@@ -39,6 +41,10 @@ class OracleEvents:
             rows = [(r, l, h) for r in range(self.B) for l in range(s.L) for h in range(s.Hkv)]
         self.rows = list(rows)
         self.reqs = sorted({r for r, _, _ in self.rows})
+        per_req = {}
+        for r, _, _ in self.rows:
+            per_req[r] = per_req.get(r, 0) + 1
+        self.full_reqs = [r for r in self.reqs if per_req[r] == s.L * s.Hkv]
         self.bt = wl.block_table.cpu().numpy().copy()
         self.P = wl.num_pages.cpu().numpy().astype(np.int32).copy()
         self.N = self.P.astype(np.int64) * s.b
@@ -94,19 +100,18 @@ class OracleEvents:
         ks = {key: int(v.dp[0]) for key, v in res.items()}
         kl = {key: int(v.dp[1]) for key, v in res.items()}
         out = dict(ks=ks, kl=kl)
-        if self.all_rows:
-            decision = np.zeros(self.B, dtype=np.int8)
-            diff = np.zeros(self.B, dtype=np.int64)
-            delta = np.zeros(self.B, dtype=np.float64)
-            for r in range(self.B):
-                a = np.array([ks[(r, l, h)] for l in range(cfg.L) for h in range(cfg.Hkv)],
-                             dtype=np.int32)
-                c = np.array([kl[(r, l, h)] for l in range(cfg.L) for h in range(cfg.Hkv)],
-                             dtype=np.int32)
-                decision[r], diff[r], delta[r] = oracle.decide(cfg, a, c,
-                                                               (int(self.P[r]) - 1) * cfg.b)
-            out.update(decision=decision, diff=diff, delta=delta)
-        else:
+        decision = np.zeros(self.B, dtype=np.int8)
+        diff = np.zeros(self.B, dtype=np.int64)
+        delta = np.zeros(self.B, dtype=np.float64)
+        for r in self.full_reqs:
+            a = np.array([ks[(r, l, h)] for l in range(cfg.L) for h in range(cfg.Hkv)],
+                         dtype=np.int32)
+            c = np.array([kl[(r, l, h)] for l in range(cfg.L) for h in range(cfg.Hkv)],
+                         dtype=np.int32)
+            decision[r], diff[r], delta[r] = oracle.decide(cfg, a, c,
+                                                           (int(self.P[r]) - 1) * cfg.b)
+        out.update(decision=decision, diff=diff, delta=delta)
+        if not self.all_rows:
             decision = np.asarray(decision_override, dtype=np.int8)
         action, self.free_count, counters = oracle.grow(decision, self.bt, self.P,
                                                         self.free_stack, self.free_count, reserve)

@@ -4,21 +4,20 @@ query / 8 KV heads, d 128), page counts uniform in [4, 128], pages
 interleaved in a 5120-page pool, free pages for about a third of the growing
 requests, one boundary event for all 64 requests.
 
-The oracle cannot score all 16384 (request, layer, KV head) rows within a
-test, so it checks a seeded sample of rows one by one, bit for bit: both
-D_p values (§3.2 Eq. 2 and Eq. 7), the dropped slots of Eq. 10 and the
-compacted K/V bytes.  Its summaries come from running A0 on the sampled
-layers only (the update is independent per layer).  Everything else is
-checked by properties that hold at any size: the decision is Eq. 8's sign
-rule over the request's own D_p values (tau = 0), pages go to the Grow
-requests in request order from the top of the free stack while the pool
-lasts and the rest fall back (§3.2, App. E.2), every compressing request
-ends one page of slots shorter and every growing request keeps its bytes.
+Every one of the 16384 (request, layer, KV head) rows is checked against the
+oracle, bit for bit: the summaries after the query stream (A0), both D_p
+values of every row (§3.2 Eq. 2 and Eq. 7), each request's Delta, integer
+difference and decision from the oracle's own D_p (Eq. 8), the page grants
+and fallbacks in request order (§3.3, §4.2), the dropped slots of every
+compressing row (§3.3 Eq. 10) and every K/V byte each row holds afterwards:
+the kept rows in slot order for a compressing request, the untouched rows
+for a growing one.  The oracle runs one layer at a time on host copies
+(tests/batch_oracle.py), keeping digests of the expected bytes.
 The decode step over the same batch (all 32 layers, as the benchmark runs
-it) is checked the same way: sampled (request, layer, KV head) outputs
-against the fp64 definition of §3.1 Eq. 3, and the summaries it updates on
-the sampled layers bit for bit against A0.  Citations are to "GrowPage:
-On-Demand KV Budgeting for Efficient LLM Reasoning Serving"."""
+it) is checked on sampled (request, layer, KV head) outputs against the fp64
+definition of §3.1 Eq. 3, and the summaries it updates on the sampled layers
+bit for bit against A0.  Citations are to "GrowPage: On-Demand KV Budgeting
+for Efficient LLM Reasoning Serving"."""
 import dataclasses
 import gc
 
@@ -29,7 +28,9 @@ import torch
 import oracle
 from paged_kv_cache_04_amd import synth
 from paged_kv_cache_04_amd.runner import DecodeRunner
-from gpu_util import device_rows, gb_config, log, oracle_config, run_stream_gpu, runner_for
+from batch_oracle import StreamedBatchOracle
+from gpu_util import (device_rows, gb_config, log, oracle_config, run_stream_gpu,
+                      run_stream_oracle, runner_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,118 +42,79 @@ ROWS_PER_REQUEST = 2
 
 
 @needs_gpu
-def test_batch64_full_size_sampled_rows():
-    log("test_batch64_full_size_sampled_rows")
+@pytest.mark.timeout(900)
+def test_batch64_full_size_every_row():
+    log("test_batch64_full_size_every_row")
     gc.collect()
     torch.cuda.empty_cache()
     wl = synth.batch64("cuda", pool_pages=POOL_PAGES)
     s = wl.shape
-    G = s.Hq // s.Hkv
     cfg = gb_config(s, max_slots=wl.max_slots)
     ocfg = oracle_config(cfg)
-    B = wl.B
+    B, b, R = wl.B, ocfg.b, ocfg.R
     bt0 = wl.block_table.cpu().numpy().copy()
     P0 = wl.num_pages.cpu().numpy().astype(np.int64)
     fs0 = wl.free_stack.cpu().numpy().copy()
     fc0 = int(wl.free_count.item())
     slot = wl.slot.cpu().numpy()
-    pos = wl.position.cpu().numpy()
-    rope = wl.rope.cpu().numpy()
-    b, R = ocfg.b, ocfg.R
-
-    rng = np.random.default_rng(6464)
-    layers = np.sort(rng.choice(s.L, SAMPLE_LAYERS, replace=False))
-    sample = [(r, int(rng.choice(layers)), int(rng.integers(s.Hkv)))
-              for r in range(B) for _ in range(ROWS_PER_REQUEST)]
-    pre = {}
-    for r, l, h in sample:
-        pages = bt0[r, :P0[r]]
-        pre[(r, l, h)] = (device_rows(wl.k_pool, l, h, pages), device_rows(wl.v_pool, l, h, pages))
-    log(f"  {len(sample)} sampled rows over layers {layers.tolist()}, "
-        f"{int(P0.sum())} pages in use, {fc0} free")
+    log(f"  {int(P0.sum())} pages in use, {fc0} free, {B * s.L * s.Hkv} rows")
 
     run = runner_for(wl, cfg, want_abar=False, want_dropped=True)
     q_cur = run_stream_gpu(run, wl)
+    torch.cuda.synchronize()
+    # A0 over the whole stream, every layer, against the oracle
+    state, q_last = run_stream_oracle(wl, ocfg)
+    got_state = run.qstate.cpu().numpy()
+    assert np.array_equal(got_state[:, slot].view(np.uint32), state[:, slot].view(np.uint32))
+    del got_state
+    log("  summaries bit-exact")
+
+    ref = StreamedBatchOracle(ocfg, wl, state, q_last, bt0, P0, log=log)
+    ref.before()
+
     run.demand(q_cur)
     run.grow()
     run.compress()
     torch.cuda.synchronize()
     assert run.device_errors() == 0
 
-    # the oracle's summaries of the sampled layers (A0 acts per layer)
-    ocfg_s = dataclasses.replace(ocfg, L=SAMPLE_LAYERS)
-    state = np.zeros((SAMPLE_LAYERS, wl.max_slots, 2, s.Hq, s.d), np.float32)
-    lidx = torch.as_tensor(layers, device="cuda")
-    qs = None
-    for t in range(wl.steps):
-        qs = wl.query(t).index_select(1, lidx).cpu().numpy()
-        oracle.ema(ocfg_s, state, qs, slot, wl.first_step(t).cpu().numpy())
-
     o = run.out
-    ks = o.k_short.cpu().numpy()
-    kl = o.k_long.cpu().numpy()
-    diff = o.k_diff.cpu().numpy()
-    decision = o.decision.cpu().numpy()
+    np.testing.assert_array_equal(o.k_short.cpu().numpy(), ref.ks)
+    np.testing.assert_array_equal(o.k_long.cpu().numpy(), ref.kl)
+    want = ref.decide_and_grow(fs0, fc0)
+    np.testing.assert_array_equal(o.k_diff.cpu().numpy(), want["diff"])
+    np.testing.assert_array_equal(o.delta.cpu().numpy(), want["delta"])
+    np.testing.assert_array_equal(o.decision.cpu().numpy(), want["decision"])
     action = run.action.cpu().numpy()
-    bt = run.batch.block_table.cpu().numpy()
-    P = run.batch.num_pages.cpu().numpy()
-    nt = run.batch.num_tokens.cpu().numpy()
+    np.testing.assert_array_equal(action, want["action"])
+    np.testing.assert_array_equal(run.batch.block_table.cpu().numpy(), want["bt"])
+    np.testing.assert_array_equal(run.batch.num_pages.cpu().numpy(), want["P"])
+    assert int(wl.free_count.item()) == want["free_count"]
+    c = run.counters()
+    assert (c["grown"], c["compress"], c["fallback"]) == tuple(int(x) for x in want["counters"])
+    grown = action == oracle.GROW
+    fallback = (want["decision"] == oracle.GROW) & ~grown
+    log(f"  D_p of every row, decisions and grants match: {int(grown.sum())} grown, "
+        f"{int(fallback.sum())} fell back, "
+        f"{int((want['decision'] == oracle.COMPRESS).sum())} chose Compress & Hold")
+    assert grown.any() and fallback.any() and (want["decision"] == oracle.COMPRESS).any()
+    np.testing.assert_array_equal(run.batch.num_tokens.cpu().numpy(),
+                                  np.where(grown, P0 * b, (P0 - 1) * b))
+
     dropped = run.dropped.cpu().numpy()
-
-    # Eq. 8 at tau = 0 over each request's own D_p values
-    want_diff = (ks.astype(np.int64) - kl.astype(np.int64)).sum(axis=(1, 2))
-    assert np.array_equal(diff, want_diff)
-    assert np.array_equal(decision, np.where(want_diff > 0, oracle.GROW, oracle.COMPRESS))
-    # grant in request order from the top of the free stack, then fallback
-    fc = fc0
-    want_action = np.zeros(B, np.int8)
-    want_bt, want_P = bt0.copy(), P0.copy()
     for r in range(B):
-        if decision[r] == oracle.GROW and fc > 0:
-            fc -= 1
-            want_bt[r, want_P[r]] = fs0[fc]
-            want_P[r] += 1
-            want_action[r] = 1
-    assert np.array_equal(action, want_action)
-    assert np.array_equal(P, want_P) and np.array_equal(bt, want_bt)
-    assert int(wl.free_count.item()) == fc
-    grown = action == 1
-    fallback = (decision == oracle.GROW) & ~grown
-    log(f"  {int(grown.sum())} grown, {int(fallback.sum())} fell back, "
-        f"{int((decision == oracle.COMPRESS).sum())} chose Compress & Hold")
-    assert grown.any() and fallback.any() and (decision == oracle.COMPRESS).any()
-    assert np.array_equal(nt, np.where(grown, P0 * b, (P0 - 1) * b))
-
-    # sampled rows against the oracle, bit for bit
-    qh_cache = {}
-    n_comp = 0
-    for r, l, h in sample:
-        if r not in qh_cache:
-            qh_cache[r] = oracle.qhat(ocfg_s, state, int(slot[r]), qs[r], rope[int(pos[r])])
-        li = int(np.searchsorted(layers, l))
-        q2 = np.ascontiguousarray(qh_cache[r][li][:, h * G:(h + 1) * G])
-        k_pre, v_pre = pre[(r, l, h)]
-        res = oracle.row(ocfg, k_pre, q2)
-        assert (ks[r, l, h], kl[r, l, h]) == (res.dp[0], res.dp[1]), (r, l, h)
-        N = int(P0[r]) * b
-        if grown[r]:
-            assert np.all(dropped[r, l, h] == -1)
-            assert np.array_equal(device_rows(wl.k_pool, l, h, bt0[r, :P0[r]]), k_pre), (r, l, h)
-            assert np.array_equal(device_rows(wl.v_pool, l, h, bt0[r, :P0[r]]), v_pre), (r, l, h)
-            continue
-        n_comp += 1
-        keep = oracle.select(ocfg, res.abar_all)
-        want_drop = np.nonzero(keep[:N - R] == 0)[0]
-        assert np.array_equal(dropped[r, l, h, :b], want_drop), (r, l, h)
-        kw, vw = k_pre.copy(), v_pre.copy()
-        n = oracle.compact(kw, keep)
-        oracle.compact(vw, keep)
-        assert n == N - b
-        kg = device_rows(wl.k_pool, l, h, bt[r, :P[r]])[:n]
-        vg = device_rows(wl.v_pool, l, h, bt[r, :P[r]])[:n]
-        assert np.array_equal(kg, kw[:n]) and np.array_equal(vg, vw[:n]), (r, l, h)
-    log(f"  {len(sample)} rows match ({n_comp} compacted)")
-    del run, wl, pre
+        for l in range(s.L):
+            for h in range(s.Hkv):
+                if grown[r]:
+                    assert np.all(dropped[r, l, h] == -1), (r, l, h)
+                else:
+                    np.testing.assert_array_equal(dropped[r, l, h, :b], ref.dropped[(r, l, h)],
+                                                  err_msg=str((r, l, h)))
+    log("  dropped slots of every compressing row match")
+    n_comp, n_grow = ref.after(action)
+    log(f"  K/V bytes of {n_comp} compacted and {n_grow} untouched rows match")
+    ref.copier.release()
+    del run, wl, ref
     gc.collect()
     torch.cuda.empty_cache()
 

@@ -11,8 +11,10 @@ compacted K/V), so every event also checks the previous ones' results.
     slots and every byte of the compacted K and V.
   * Qwen3-8B shape, 16 requests of 32768 tokens in a pool with no free page,
     8 successive events: every request falls back to Compress & Hold.  The
-    oracle follows 12 sampled rows (D_p, dropped slots, compacted K/V); the
-    decision outputs of all rows are checked for consistency with the GPU's
+    oracle follows every row of two requests (all 36 x 8 rows: D_p, Delta,
+    the integer difference and the decision of Eq. 8, dropped slots,
+    compacted K/V) and 6 sampled rows of two others; the decision outputs
+    of the remaining requests are checked for consistency with the GPU's
     own D_p.
 """
 import numpy as np
@@ -111,6 +113,7 @@ def test_qwen16k_ten_events_delta_changes_sign():
 
 
 @needs_gpu
+@pytest.mark.timeout(600)
 def test_qwen32k_stress_successive_compress_and_hold():
     log("test_qwen32k_stress_successive_compress_and_hold")
     events, warm, gap = 8, 512, synth.EVENT_GAP
@@ -119,9 +122,12 @@ def test_qwen32k_stress_successive_compress_and_hold():
     cfg = gb_config(s, max_slots=wl.max_slots)
     rng = np.random.default_rng(11)
     reqs = rng.choice(wl.B, size=4, replace=False)
-    rows = [(int(r), int(rng.integers(s.L)), int(rng.integers(s.Hkv))) for r in reqs
-            for _ in range(3)]
+    full = sorted(int(r) for r in reqs[:2])
+    rows = [(r, l, h) for r in full for l in range(s.L) for h in range(s.Hkv)]
+    rows += [(int(r), int(rng.integers(s.L)), int(rng.integers(s.Hkv))) for r in reqs[2:]
+             for _ in range(3)]
     sim = OracleEvents(oracle_config(cfg), wl, rows=rows)
+    assert sim.full_reqs == full
     qstate = torch.zeros((s.L, wl.max_slots, 2, s.Hq, s.d), dtype=torch.float32, device="cuda")
     LH = s.L * s.Hkv
     t_from = 0
@@ -146,6 +152,12 @@ def test_qwen32k_stress_successive_compress_and_hold():
                                       diff.astype(np.float64) / (float(LH) * card))
         np.testing.assert_array_equal(run.out.decision.cpu().numpy(),
                                       (run.out.delta.cpu().numpy() > 0).astype(np.int8))
+        # the fully followed requests: Eq. 8 from the oracle's own D_p
+        for r in full:
+            assert run.out.k_diff.cpu().numpy()[r] == ref["diff"][r], (e, r)
+            assert run.out.delta.cpu().numpy()[r] == ref["delta"][r], (e, r)
+            assert run.out.decision.cpu().numpy()[r] == ref["decision"][r], (e, r)
+        log(f"    requests {full}: delta {[float(ref['delta'][r]) for r in full]}")
         _check_rows(wl, run, sim, ref, rows, action)
         np.testing.assert_array_equal(wl.num_tokens.cpu().numpy(), (card).astype(np.int32))
         _append(wl, sim, e)

@@ -3,8 +3,10 @@ KV Budgeting for Efficient LLM Reasoning Serving"): after the grant step,
 the requests taking Compress & Hold are compressed on a second stream while
 the other requests (here the ones that grew) run a decode step on the first.
 The two touch disjoint pages, summary slots and workspaces, so the results
-must be bit-identical to running the two one after the other; the decode
-outputs are also checked against the fp64 definition."""
+must be bit-identical to running the two one after the other.  Both are also
+checked against the oracle: the decisions and grants, the dropped slots of
+every compressing row and its compacted K/V bytes (§3.3 Eq. 10) bit for bit,
+the decode outputs within tolerance of the fp64 definition (§3.1 Eq. 3)."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +14,8 @@ import torch
 import oracle
 from paged_kv_cache_04_amd import synth
 from paged_kv_cache_04_amd.runner import DecodeRunner, sub_batch
-from gpu_util import HostCopy, gb_config, log, run_stream_gpu, runner_for
+from gpu_util import (HostCopy, device_rows, gb_config, log, oracle_config, oracle_event,
+                      run_stream_gpu, run_stream_oracle, runner_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +89,29 @@ def test_compression_on_second_stream_matches_serial():
     nt = serial["nt"].cpu().numpy()
     N0 = np.array(P) * MID.b
     assert np.array_equal(nt[comp], N0[comp] - MID.b) and np.array_equal(nt[dec_rows], N0[dec_rows])
+    # the compression against the oracle, bit for bit
+    ocfg = oracle_config(cfg)
+    state, qcur = run_stream_oracle(wl, ocfg)
+    ref = oracle_event(ocfg, hc, state, qcur)
+    np.testing.assert_array_equal(ref["action"], action)
+    dropped = serial["dropped"].cpu().numpy()
+    bt = run.batch.block_table.cpu().numpy()
+    n_rows = 0
+    for r in comp:
+        for l in range(MID.L):
+            for h in range(MID.Hkv):
+                key = (int(r), l, h)
+                np.testing.assert_array_equal(dropped[r, l, h, :MID.b], ref["dropped"][key],
+                                              err_msg=str(key))
+                k_want, v_want = ref["compacted"][key]
+                n = k_want.shape[0]
+                pages = bt[r, :hc.P[r]]
+                for name in ("k", "v"):
+                    got = device_rows(serial[name], l, h, pages)[:n]
+                    want = k_want if name == "k" else v_want
+                    np.testing.assert_array_equal(got, want, err_msg=f"{name} {key}")
+                n_rows += 1
+    log(f"  {n_rows} compressed rows match the oracle")
     # decode outputs against the fp64 definition
     out = serial["out"].cpu().numpy()
     qn = q_dec.cpu().numpy()
