@@ -223,7 +223,8 @@ struct DemandArgs {
 };
 
 __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __restrict__ qhat,
-                                               const uint16_t* __restrict__ k_pool) {
+                                               const uint16_t* __restrict__ k_pool,
+                                               const int32_t* __restrict__ block_table) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ float s_wmax[kDW][2][kNQ];
   __shared__ float s_m[2][kNQ];
@@ -267,37 +268,48 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     const float* __restrict__ qv = qhat + (int64_t)row * (kNQ * kD);
 
     // ---- 1. score -------------------------------------------------------------
+    // A tile's 8 logits per key are stored one tile late, right after the
+    // loads of the next half are issued, so that no wait for key loads ever
+    // covers a ring store (vector loads and stores share one in-order
+    // counter).  A key of the newest page belongs to a wave's last tile, so
+    // the maxima over C_t run over the earlier tiles and the last one is
+    // sorted after the loop.
     float md[kNQ], ml[kNQ];
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) md[q] = ml[q] = -INFINITY;
     const int n_tiles = (int)(4 * P);
     if (w < n_tiles) {
-      auto tile_base = [&](int tt, bool& bad) -> const unsigned char* {
-        const int pg = tt >> 2;
-        const int page = a.block_table[(int64_t)r * a.max_pages + pg];
+      const int32_t* __restrict__ bt_row = block_table + (int64_t)r * a.max_pages;
+      // lane part of a key load: key lane >> 3 of each group of 8, 16 bytes
+      // (lane & 7) of its half row
+      const uint32_t lane_off = (uint32_t)((lane >> 3) * 256 + (lane & 7) * 16);
+      auto tile_base = [&](int tt, int page, bool& bad) -> const unsigned char* {
         bad = page < 0 || page >= a.pool_pages;
         return reinterpret_cast<const unsigned char*>(
             k_pool + ((((int64_t)l * a.pool_pages + (bad ? 0 : page)) * a.Hkv + h) * kPage +
                         (tt & 3) * 64) * kD);
       };
       auto issue = [&](const unsigned char* base, int half, u32x4* v) {
+        const unsigned char* p = base + lane_off + half * 128;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = i * 8 + (lane >> 3);
-          v[i] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(base + key * 256 + half * 128 + (lane & 7) * 16));
-        }
+        for (int i = 0; i < 8; ++i)
+          v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * 2048));
       };
       int tt = w;
       bool bad;
-      const unsigned char* src = tile_base(tt, bad);
+      const unsigned char* src = tile_base(tt, bt_row[tt >> 2], bad);
       u32x4 v[8];
       issue(src, 0, v);
+      float pacc[kNQ];  // logits of the previous tile, stored during this one
+#pragma unroll
+      for (int qi = 0; qi < kNQ; ++qi) pacc[qi] = 0.0f;
+      int ptile = tt;  // the first round stores zeros into its own tile's slot
       while (true) {
         const int tcur = tt;
         const bool cur_bad = bad;
         const unsigned char* cur_src = src;
-        bool has_next = false;
+        const bool has_next = tt + kDW < n_tiles;
+        const int next_page = has_next ? bt_row[(tt + kDW) >> 2] : 0;
         float acc[kNQ];
 #pragma unroll
         for (int qi = 0; qi < kNQ; ++qi) acc[qi] = 0.0f;
@@ -311,13 +323,13 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
           wave_order();
           if (half == 0) {
             issue(cur_src, 1, v);
-          } else {
-            has_next = tt + kDW < n_tiles;
-            if (has_next) {
-              tt += kDW;
-              src = tile_base(tt, bad);
-              issue(src, 0, v);
-            }
+            float4* out = reinterpret_cast<float4*>(lg + (int64_t)ptile * (64 * kNQ)) + lane;
+            out[0] = make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+            out[64] = make_float4(pacc[4], pacc[5], pacc[6], pacc[7]);
+          } else if (has_next) {
+            tt += kDW;
+            src = tile_base(tt, next_page, bad);
+            issue(src, 0, v);
           }
           if (!cur_bad) {
             const unsigned char* rowp = my + lane * kHalfPad;
@@ -346,17 +358,24 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
           wave_order();
         }
         if (cur_bad && lane == 0) atomicOr(a.err, GP_DEVERR_PAGE);
-        float4* out = reinterpret_cast<float4*>(lg + (int64_t)tcur * (64 * kNQ)) + lane;
-        out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        out[64] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        if ((tcur >> 2) < P - 1) {
+        if (ptile != tcur) {  // the previous tile lies in C_t (it is not a wave's last)
 #pragma unroll
-          for (int q = 0; q < kNQ; ++q) md[q] = fmaxf(md[q], acc[q]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < kNQ; ++q) ml[q] = fmaxf(ml[q], acc[q]);
+          for (int q = 0; q < kNQ; ++q) md[q] = fmaxf(md[q], pacc[q]);
         }
+#pragma unroll
+        for (int qi = 0; qi < kNQ; ++qi) pacc[qi] = acc[qi];
+        ptile = tcur;
         if (!has_next) break;
+      }
+      float4* out = reinterpret_cast<float4*>(lg + (int64_t)ptile * (64 * kNQ)) + lane;
+      out[0] = make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+      out[64] = make_float4(pacc[4], pacc[5], pacc[6], pacc[7]);
+      if ((ptile >> 2) < P - 1) {
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) md[q] = fmaxf(md[q], pacc[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) ml[q] = pacc[q];
       }
     }
 #pragma unroll
@@ -658,7 +677,8 @@ hipError_t launch_demand(const Params& p, const WsLayout& w, const uint16_t* k_p
   a.k_long = k_long;
   a.abar = abar;
   a.err = err;
-  hipLaunchKernelGGL(k_demand, dim3((unsigned)w.blocks), dim3(kDT), 0, s, a, a.qhat, a.k_pool);
+  hipLaunchKernelGGL(k_demand, dim3((unsigned)w.blocks), dim3(kDT), 0, s, a, a.qhat, a.k_pool,
+                     a.block_table);
   return hipGetLastError();
 }
 
