@@ -29,6 +29,10 @@ SYMBOLS = (
     "gp_decode_workspace_bytes", "gp_decode_attention",
 )
 
+# bandwidth probes (include/gp_probe.h)
+PROBE_SYMBOLS = ("gp_probe_read", "gp_probe_copy")
+GP_PROBE_BLOCK_BYTES = 16384
+
 KERNELS = ("ema", "plan", "qhat", "demand", "decide", "grow", "select", "compact", "return",
            "share", "decode")
 
@@ -118,6 +122,10 @@ def load(path: str = LIB_PATH):
     L.gp_decode_attention.argtypes = [vp, ctypes.POINTER(gp_pool), ctypes.POINTER(gp_batch), i32,
                                       vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.gp_decode_attention.restype = ctypes.c_int
+    L.gp_probe_read.argtypes = [vp, sz, vp, vp]
+    L.gp_probe_read.restype = ctypes.c_int
+    L.gp_probe_copy.argtypes = [vp, vp, sz, vp]
+    L.gp_probe_copy.restype = ctypes.c_int
     L.gp_get_counters.argtypes = [vp, ctypes.POINTER(gp_counters)]
     L.gp_get_counters.restype = ctypes.c_int
     L.gp_get_device_errors.argtypes = [vp, ctypes.POINTER(i32)]
@@ -314,6 +322,23 @@ def gp_decode_attention(ctx: Context, pool: Pool, batch: Batch, layer: int, q, q
                                       int(rope.shape[0]), _ptr(out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "gp_decode_attention", ctx)
+
+
+def gp_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Streaming read of every byte of src (include/gp_probe.h)."""
+    rc = load().gp_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                              _stream(stream))
+    if rc != 0:
+        raise GPError(f"gp_probe_read: HIP error {rc}")
+
+
+def gp_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Streaming copy of src into dst (include/gp_probe.h)."""
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    rc = load().gp_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream))
+    if rc != 0:
+        raise GPError(f"gp_probe_copy: HIP error {rc}")
 
 
 def gp_get_counters(ctx: Context) -> dict:

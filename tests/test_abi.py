@@ -27,6 +27,19 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(gb.SYMBOLS)
 
 
+def test_library_exports_the_probe_header():
+    src = open(os.path.join(ROOT, "include", "gp_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(gp_[a-z_]+)\s*\(", src)))
+    assert names == sorted(gb.PROBE_SYMBOLS)
+    lib = gb.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    # host-side refusals: sizes that are not whole 16 KiB blocks, null pointers
+    assert lib.gp_probe_read(None, 16384, None, None) != 0
+    assert lib.gp_probe_copy(16, 32, 100, None) != 0
+
+
 def test_status_strings_and_invalid_config():
     lib = gb.load()
     assert lib.gp_status_str(0) == b"ok"
