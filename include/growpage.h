@@ -295,6 +295,32 @@ gp_status gp_decode_attention(gp_ctx* ctx, const gp_pool* pool, const gp_batch* 
                               float* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Size of the library's static scratch buffer (one per GPU). */
+#define GP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * gp_decode_attention with its scratch (rotated queries, work list, per-run
+ * partials) in a buffer the library holds instead of a caller workspace.
+ * Same kernels and arguments as gp_decode_attention minus the workspace, and
+ * the same outputs bit for bit.
+ *  - The buffer is GP_STATIC_SCRATCH_BYTES (64 MiB) of device memory per GPU,
+ *    set up by gp_create on its device and held until the process ends.
+ *  - A batch whose gp_decode_workspace_bytes(ctx, B, sum of num_pages_host)
+ *    exceeds GP_STATIC_SCRATCH_BYTES is refused with GP_ERR_WORKSPACE before
+ *    anything is enqueued (with 8 KV heads: about 4000 cached pages, about a
+ *    million tokens, per call).
+ *  - All calls on one GPU share the buffer, which keeps the last call's
+ *    contents (nothing in it needs clearing: every call writes what it
+ *    reads).  Calls that overlap in time on one GPU (on different streams,
+ *    or from several contexts or host threads) race on it: order them on one
+ *    stream.
+ *  - Allocates nothing and records no gp_profile events. */
+gp_status gp_decode_attention_static(gp_ctx* ctx, const gp_pool* pool, const gp_batch* batch,
+                                     int32_t layer, const float* q, float* qstate,
+                                     const uint8_t* first_step, const float* rope,
+                                     int32_t rope_rows, float* out, void* stream);
+
 /* Kernels of the event, for gp_profile_read. */
 enum gp_kernel_id {
   GP_K_EMA = 0,     /* A0 summary update */

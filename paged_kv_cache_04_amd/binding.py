@@ -26,8 +26,11 @@ SYMBOLS = (
     "gp_create", "gp_destroy", "gp_workspace_bytes", "gp_update_summaries", "gp_demand",
     "gp_grow_page", "gp_compress_hold", "gp_get_counters", "gp_get_device_errors",
     "gp_status_str", "gp_last_hip_error", "gp_profile", "gp_profile_read",
-    "gp_decode_workspace_bytes", "gp_decode_attention",
+    "gp_decode_workspace_bytes", "gp_decode_attention", "gp_decode_attention_static",
 )
+
+# bytes of the library's per-GPU scratch buffer (gp_decode_attention_static)
+GP_STATIC_SCRATCH_BYTES = 64 << 20
 
 # bandwidth probes (include/gp_probe.h)
 PROBE_SYMBOLS = ("gp_probe_read", "gp_probe_copy")
@@ -122,6 +125,10 @@ def load(path: str = LIB_PATH):
     L.gp_decode_attention.argtypes = [vp, ctypes.POINTER(gp_pool), ctypes.POINTER(gp_batch), i32,
                                       vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.gp_decode_attention.restype = ctypes.c_int
+    L.gp_decode_attention_static.argtypes = [vp, ctypes.POINTER(gp_pool),
+                                             ctypes.POINTER(gp_batch), i32, vp, vp, vp, vp,
+                                             i32, vp, vp]
+    L.gp_decode_attention_static.restype = ctypes.c_int
     L.gp_probe_read.argtypes = [vp, sz, vp, vp]
     L.gp_probe_read.restype = ctypes.c_int
     L.gp_probe_copy.argtypes = [vp, vp, sz, vp]
@@ -322,6 +329,17 @@ def gp_decode_attention(ctx: Context, pool: Pool, batch: Batch, layer: int, q, q
                                       int(rope.shape[0]), _ptr(out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "gp_decode_attention", ctx)
+
+
+def gp_decode_attention_static(ctx: Context, pool: Pool, batch: Batch, layer: int, q, qstate,
+                               first_step, rope, out, stream=None):
+    """gp_decode_attention with the scratch in the library's per-GPU buffer
+    (no workspace argument; allocates nothing)."""
+    p, b = pool.c(), batch.c()
+    _check(load().gp_decode_attention_static(ctx.handle, ctypes.byref(p), ctypes.byref(b),
+                                             int(layer), _ptr(q), _ptr(qstate), _ptr(first_step),
+                                             _ptr(rope), int(rope.shape[0]), _ptr(out),
+                                             _stream(stream)), "gp_decode_attention_static", ctx)
 
 
 def gp_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None):

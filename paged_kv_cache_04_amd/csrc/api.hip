@@ -2,11 +2,42 @@
 // carving and launch sequencing.  Kernels live in the k_*.hip files.
 // Citations are to "GrowPage: On-Demand KV Budgeting for Efficient LLM
 // Reasoning Serving" (arXiv 2609.03494).
+#include <mutex>
 #include <new>
 #include <tuple>
 #include <vector>
 
 #include "gp_internal.h"
+
+// Scratch of gp_decode_attention_static: one copy per GPU the library runs
+// on, held until the process ends.  In host code the name below stands for
+// the array only symbolically; the device address of each GPU's copy comes
+// from hipGetSymbolAddress (scratch_address) and only that address is used.
+static __device__ __align__(256) unsigned char scratch[GP_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on `device`, which must be the current device;
+// looked up once per device.
+hipError_t scratch_address(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_dev[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[device] = ptr;
+  }
+  *out = g_scratch_dev[device];
+  return hipSuccess;
+}
+
+}  // namespace
 
 struct gp_ctx {
   gp::Params p;
@@ -15,6 +46,7 @@ struct gp_ctx {
   int64_t* d_counters = nullptr;  // [5]: granted, compress, fallback, returned, copied
   int32_t* d_err = nullptr;       // [1], right after the counters
   int last_hip = 0;
+  void* scratch = nullptr;  // this device's copy of `scratch` (gp_decode_attention_static)
   // bookkeeping of the last gp_demand, checked by gp_compress_hold
   const void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -87,6 +119,33 @@ gp_status check_batch(const gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
   return GP_OK;
 }
 
+// gp_decode_attention and its static-scratch variant: validation, then the
+// three decode kernels on `ws` (at least ws_bytes long).  With profile
+// false no HIP event is created or recorded.
+gp_status decode_call(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, int32_t layer,
+                      const float* q, float* qstate, const uint8_t* first_step, const float* rope,
+                      int32_t rope_rows, float* out, void* ws, size_t ws_bytes, void* stream,
+                      bool profile) {
+  if (!c || !q || !rope || rope_rows < 1 || !out || !ws) return GP_ERR_INVALID_ARG;
+  if (!shape_supported(c->p)) return GP_ERR_UNSUPPORTED;
+  if (layer < 0 || layer >= c->p.L) return GP_ERR_INVALID_ARG;
+  int64_t total_pages = 0, max_pages_used = 0;
+  gp_status st = check_batch(c, pool, bt, &total_pages, &max_pages_used);
+  if (st != GP_OK) return st;
+  const gp::DecodeWs w = gp::decode_ws_layout(c->p, bt->batch, total_pages);
+  if (ws_bytes < w.total) return GP_ERR_WORKSPACE;
+  if (w.unit_cap > INT32_MAX) return GP_ERR_UNSUPPORTED;
+  const int unit_blocks = c->num_cus * GP_DECODE_BLOCKS_PER_CU;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto launch = [&] {
+    return gp::launch_decode(c->p, w, bt->batch, layer, pool->k_pool, pool->v_pool,
+                             pool->num_pages, bt->block_table, bt->max_pages, bt->num_pages,
+                             bt->num_tokens, bt->slot, bt->position, q, qstate, first_step, rope,
+                             rope_rows, unit_blocks, ws, out, c->d_err, s);
+  };
+  return hip_fail(c, profile ? timed(c, GP_K_DECODE, s, launch) : launch());
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,6 +189,7 @@ gp_status gp_create(const gp_config* cfg, gp_ctx** out) {
     e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&c->d_counters), 64);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, 64);
+  if (e == hipSuccess) e = scratch_address(c->device, &c->scratch);
   if (e != hipSuccess) {
     if (c->d_counters) (void)hipFree(c->d_counters);
     delete c;
@@ -302,23 +362,17 @@ gp_status gp_decode_attention(gp_ctx* c, const gp_pool* pool, const gp_batch* bt
                               const float* q, float* qstate, const uint8_t* first_step,
                               const float* rope, int32_t rope_rows, float* out, void* ws,
                               size_t ws_bytes, void* stream) {
-  if (!c || !q || !rope || rope_rows < 1 || !out || !ws) return GP_ERR_INVALID_ARG;
-  if (!shape_supported(c->p)) return GP_ERR_UNSUPPORTED;
-  if (layer < 0 || layer >= c->p.L) return GP_ERR_INVALID_ARG;
-  int64_t total_pages = 0, max_pages_used = 0;
-  gp_status st = check_batch(c, pool, bt, &total_pages, &max_pages_used);
-  if (st != GP_OK) return st;
-  const gp::DecodeWs w = gp::decode_ws_layout(c->p, bt->batch, total_pages);
-  if (ws_bytes < w.total) return GP_ERR_WORKSPACE;
-  if (w.unit_cap > INT32_MAX) return GP_ERR_UNSUPPORTED;
-  const int unit_blocks = c->num_cus * GP_DECODE_BLOCKS_PER_CU;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_fail(c, timed(c, GP_K_DECODE, s, [&] {
-    return gp::launch_decode(c->p, w, bt->batch, layer, pool->k_pool, pool->v_pool,
-                             pool->num_pages, bt->block_table, bt->max_pages, bt->num_pages,
-                             bt->num_tokens, bt->slot, bt->position, q, qstate, first_step, rope,
-                             rope_rows, unit_blocks, ws, out, c->d_err, s);
-  }));
+  return decode_call(c, pool, bt, layer, q, qstate, first_step, rope, rope_rows, out, ws,
+                     ws_bytes, stream, true);
+}
+
+gp_status gp_decode_attention_static(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
+                                     int32_t layer, const float* q, float* qstate,
+                                     const uint8_t* first_step, const float* rope,
+                                     int32_t rope_rows, float* out, void* stream) {
+  if (!c || !c->scratch) return GP_ERR_INVALID_ARG;
+  return decode_call(c, pool, bt, layer, q, qstate, first_step, rope, rope_rows, out,
+                     c->scratch, GP_STATIC_SCRATCH_BYTES, stream, false);
 }
 
 gp_status gp_profile(gp_ctx* c, int enable) {
