@@ -69,22 +69,70 @@ __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const unsigned lo = __shfl_xor((unsigned)v, m);
-  const unsigned hi = __shfl_xor((unsigned)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 __device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int off) {
   const unsigned lo = __shfl_down((unsigned)v, off);
   const unsigned hi = __shfl_down((unsigned)(v >> 32), off);
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v += shfl_xor_u64(v, m);
+// Cross-lane sums without LDS traffic: DPP rotations within each 16-lane
+// row, and gfx950's permlane swaps, which exchange the odd 16-lane rows of
+// one register with the even rows of another (permlane16) or the upper 32
+// lanes of one with the lower 32 of another (permlane32).
+__device__ __forceinline__ uint64_t pk64(uint32_t lo, uint32_t hi) {
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return pk64(lo, hi);
+}
+
+// sum over the 16 lanes of each row, in every lane of the row (row_ror 8, 4, 2, 1)
+__device__ __forceinline__ uint64_t row_sum_u64(uint64_t v) {
+  v += dpp_u64<0x128>(v);
+  v += dpp_u64<0x124>(v);
+  v += dpp_u64<0x122>(v);
+  v += dpp_u64<0x121>(v);
   return v;
+}
+
+// a + b after lanes 32..63 of a trade places with lanes 0..31 of b: lanes
+// 0..31 get a's value there plus a's value 32 lanes up, lanes 32..63 b's
+// value plus b's value 32 lanes down
+__device__ __forceinline__ uint64_t swap32_add(uint64_t a, uint64_t b) {
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)b, false, false);
+  const auto hi =
+      __builtin_amdgcn_permlane32_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+  return pk64(lo[0], hi[0]) + pk64(lo[1], hi[1]);
+}
+
+// the same with the odd 16-lane rows of a and the even rows of b
+__device__ __forceinline__ uint64_t swap16_add(uint64_t a, uint64_t b) {
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)b, false, false);
+  const auto hi =
+      __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+  return pk64(lo[0], hi[0]) + pk64(lo[1], hi[1]);
+}
+
+// sum over the wave, in every lane
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  v = row_sum_u64(v);
+  v = swap16_add(v, v);
+  return swap32_add(v, v);
+}
+
+// 16 values per lane summed over the wave, transposed: each exchange halves
+// the values a lane carries.  Lane L ends with the totals of values
+// 8 b5 + 4 b4 + j (j = 0..3) in out[j], b5 and b4 being bits 5 and 4 of L.
+__device__ __forceinline__ void wave_sum16_u64(const uint64_t (&v)[16], uint64_t (&out)[4]) {
+  uint64_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = swap32_add(v[i], v[i + 8]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = row_sum_u64(swap16_add(h[i], h[i + 4]));
 }
 
 // Wave 0: over nb buckets (cnt, mass), find the largest bucket d with
@@ -147,9 +195,14 @@ __device__ __forceinline__ float uniform_f(float v) {
 __device__ __forceinline__ float mass40(float v) { return __builtin_floorf(v * kFix); }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x124, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x122, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x121, 0xf, 0xf, false);
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] + a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] + b[1];
 }
 
 // The logits ring holds, per 64-key tile, the first four logits of its keys
@@ -443,10 +496,15 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
 #pragma unroll
         for (int q = 0; q < kNQ; ++q) zc[q] += (double)mass40(gp_exp(lv[q] - mall[q]));
       }
+      static_assert(2 * kNQ == 16, "one transposed reduction of 16 sums");
+      uint64_t zv[2 * kNQ], zs[4];
 #pragma unroll
-      for (int v = 0; v < 2 * kNQ; ++v) {
-        const uint64_t sv = wave_sum_u64((uint64_t)(v < kNQ ? zd[v] : zc[v - kNQ]));
-        if (lane == 0) s_red[w][v] = sv;
+      for (int v = 0; v < 2 * kNQ; ++v) zv[v] = (uint64_t)(v < kNQ ? zd[v] : zc[v - kNQ]);
+      wave_sum16_u64(zv, zs);
+      if ((lane & 15) == 0) {
+        const int v0 = (lane >> 5) * 8 + ((lane >> 4) & 1) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_red[w][v0 + j] = zs[j];
       }
       __syncthreads();
       if (t < 2 * kNQ) {
