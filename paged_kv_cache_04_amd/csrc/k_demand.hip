@@ -32,7 +32,8 @@
 //     then the remaining 20 bits resolved on that bucket's members only
 //     (collected into LDS, or scanned in the key ring when too many; both
 //     views in the same two passes), then
-//     D_p = (count above) + ceil(remaining mass / member mass).
+//     D_p = (count above) + ceil(remaining mass / member mass).  Each digit
+//     is found by one block-wide suffix-sum search over its buckets.
 #include "gp_internal.h"
 
 namespace gp {
@@ -48,6 +49,7 @@ constexpr int kLdsBytes = kDW * kWaveStage;   // 147456, reused after scoring
 constexpr int kH1 = 2048;                     // first-digit buckets
 constexpr int kH2 = 1024;                     // second/third-digit buckets
 constexpr int kListCap = (kLdsBytes - 2 * kH1 * 8 - 2 * kH2 * 12) / 4;  // boundary members in LDS
+constexpr int kRingU = 8;  // demand-key ring loads in flight per thread in phase 4
 constexpr int kListHalf = kListCap / 2;                            // per view
 
 // acc[qi] += q[qi][e] * k[e] for e = 0..3 in order (4 bf16 keys in k).
@@ -135,55 +137,122 @@ __device__ __forceinline__ void wave_sum16_u64(const uint64_t (&v)[16], uint64_t
   for (int i = 0; i < 4; ++i) out[i] = row_sum_u64(swap16_add(h[i], h[i + 4]));
 }
 
-// Wave 0: over nb buckets (cnt, mass), find the largest bucket d with
-// p_den * (m_above + mass of buckets >= d) >= target; returns through *d_out
-// the bucket and updates m_above / c_above to the buckets above it.
-template <int NB>
-__device__ __forceinline__ void scan_desc(const uint32_t* cnt, const uint64_t* mass,
-                                          uint64_t target, uint32_t p_den, uint64_t& m_above,
-                                          uint32_t& c_above, int& d_out) {
-  constexpr int PER = NB / 64;
-  const int lane = threadIdx.x & 63;
-  uint64_t lm = 0;
-  uint32_t lc = 0;
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  return pk64(__builtin_amdgcn_readlane((uint32_t)v, lane),
+              __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane));
+}
+
+// Inclusive suffix sums over a wave: lane L gets the sum over lanes L..63.
+// DPP row shifts (lane i reads lane i + n of its 16-lane row, 0 past the
+// row's end) give the sums within each row; then each row adds the totals of
+// the rows above it, read from their first lanes.
+__device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t v) {
+  v += dpp_u64<0x101>(v);
+  v += dpp_u64<0x102>(v);
+  v += dpp_u64<0x104>(v);
+  v += dpp_u64<0x108>(v);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint64_t r1 = readlane_u64(v, 16), r2 = readlane_u64(v, 32), r3 = readlane_u64(v, 48);
+  return v + (row < 1 ? r1 : 0) + (row < 2 ? r2 : 0) + (row < 3 ? r3 : 0);
+}
+
+__device__ __forceinline__ uint32_t wave_suffix_u32(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x101, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x102, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x104, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x108, 0xf, 0xf, false);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t r1 = __builtin_amdgcn_readlane(v, 16), r2 = __builtin_amdgcn_readlane(v, 32),
+                 r3 = __builtin_amdgcn_readlane(v, 48);
+  return v + (row < 1 ? r1 : 0u) + (row < 2 ? r2 : 0u) + (row < 3 ? r3 : 0u);
+}
+
+// Radix-digit searches of phase 4, both views at once over the whole block:
+// threads 512 x .. 512 x + 511 (waves 8 x .. 8 x + 7) take view x, each a run
+// of consecutive buckets.  A view's digit is the largest bucket d with
+// p_den * (mass above the bucket's prefix + mass of buckets >= d) >= target;
+// the mass is non-increasing in d, so exactly one bucket satisfies that and
+// has the next bucket up failing it (or is the top bucket), and the thread
+// holding it writes the digit and the mass (and count) above it.  Wave
+// suffix sums by DPP, one barrier to add the totals of the higher waves.
+static_assert(kDT == 1024, "the digit searches split the block into two views of 512 threads");
+
+// First digit: 2048 fp64 bucket masses per view (integer-valued), 4 per thread.
+__device__ __forceinline__ void block_first_digit(const double* h1m, const uint64_t* s_W,
+                                                  uint32_t p_num, uint32_t p_den,
+                                                  uint64_t* s_wm, int* s_dig, uint64_t* s_mab) {
+  static_assert(kH1 == 4 * 512, "4 buckets per thread");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, x = t >> 9, j = t & 511;
+  const double* hm = h1m + x * kH1 + 4 * j;
+  uint64_t m[4];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    lm += mass[lane * PER + u];
-    lc += cnt[lane * PER + u];
-  }
-  uint64_t sm = lm;
-  uint32_t sc = lc;
+  for (int u = 0; u < 4; ++u) m[u] = (uint64_t)hm[u];
+  const uint64_t own = m[0] + m[1] + m[2] + m[3];
+  const uint64_t suf = wave_suffix_u64(own);
+  if (lane == 0) s_wm[w] = suf;
+  __syncthreads();
+  uint64_t cum = suf - own;  // mass of the buckets above this thread's run
+  for (int ww = w + 1; ww < 8 * (x + 1); ++ww) cum += s_wm[ww];
+  const uint64_t target = s_W[x] * (uint64_t)p_num;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t vm = shfl_down_u64(sm, off);
-    const uint32_t vc = __shfl_down(sc, off);
-    if (lane + off < 64) {
-      sm += vm;
-      sc += vc;
+  for (int u = 3; u >= 0; --u) {
+    const uint64_t above = cum;
+    cum += m[u];
+    const int b = 4 * j + u;
+    if (cum * p_den >= target && (b == kH1 - 1 || above * p_den < target)) {
+      s_dig[x] = b;
+      s_mab[x] = above;
     }
   }
-  uint64_t cum = m_above + (sm - lm);
-  uint32_t ccum = c_above + (sc - lc);
-  int best = -1;
-  uint64_t best_m = 0;
-  uint32_t best_c = 0;
-  for (int u = PER - 1; u >= 0; --u) {
-    const uint64_t before = cum;
-    const uint32_t cbefore = ccum;
-    cum += mass[lane * PER + u];
-    ccum += cnt[lane * PER + u];
-    if (best < 0 && cum * (uint64_t)p_den >= target) {
-      best = lane * PER + u;
-      best_m = before;
-      best_c = cbefore;
+}
+
+// Later digits: 1024 buckets of (count, mass) per view, 2 per thread; the
+// mass and count above the bucket's prefix come in s_mab / s_cab and leave
+// updated to the new digit.
+__device__ __forceinline__ void block_next_digit(const uint32_t* h2c, const uint64_t* h2m,
+                                                 const uint64_t* s_W, uint32_t p_num,
+                                                 uint32_t p_den, uint64_t* s_wm, uint32_t* s_wc,
+                                                 int* s_dig, uint64_t* s_mab, uint32_t* s_cab) {
+  static_assert(kH2 == 2 * 512, "2 buckets per thread");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, x = t >> 9, j = t & 511;
+  const uint64_t mab0 = s_mab[x];
+  const uint32_t cab0 = s_cab[x];
+  uint64_t m[2];
+  uint32_t c[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    m[u] = h2m[x * kH2 + 2 * j + u];
+    c[u] = h2c[x * kH2 + 2 * j + u];
+  }
+  const uint64_t own_m = m[0] + m[1];
+  const uint32_t own_c = c[0] + c[1];
+  const uint64_t suf_m = wave_suffix_u64(own_m);
+  const uint32_t suf_c = wave_suffix_u32(own_c);
+  if (lane == 0) {
+    s_wm[w] = suf_m;
+    s_wc[w] = suf_c;
+  }
+  __syncthreads();
+  uint64_t cm = mab0 + (suf_m - own_m);
+  uint32_t cc = cab0 + (suf_c - own_c);
+  for (int ww = w + 1; ww < 8 * (x + 1); ++ww) {
+    cm += s_wm[ww];
+    cc += s_wc[ww];
+  }
+  const uint64_t target = s_W[x] * (uint64_t)p_num;
+#pragma unroll
+  for (int u = 1; u >= 0; --u) {
+    const uint64_t am = cm;
+    const uint32_t ac = cc;
+    cm += m[u];
+    cc += c[u];
+    const int b = 2 * j + u;
+    if (cm * p_den >= target && (b == kH2 - 1 || am * p_den < target)) {
+      s_dig[x] = b;
+      s_mab[x] = am;
+      s_cab[x] = ac;
     }
   }
-  const unsigned long long ok = __ballot(best >= 0);
-  const int hl = 63 - __clzll(ok);
-  d_out = __shfl(best, hl);
-  const unsigned lo = __shfl((unsigned)best_m, hl), hi = __shfl((unsigned)(best_m >> 32), hl);
-  m_above = ((uint64_t)hi << 32) | lo;
-  c_above = __shfl(best_c, hl);
 }
 
 __device__ __forceinline__ float uniform_f(float v) {
@@ -215,44 +284,6 @@ __device__ __forceinline__ void load_logits8(const float* lg, int64_t i, float (
   lv[4] = x1.x; lv[5] = x1.y; lv[6] = x1.z; lv[7] = x1.w;
 }
 
-// Wave 0, first radix digit: over kH1 bucket masses (integer-valued fp64,
-// exact), the largest bucket d with p_den * (mass of buckets >= d) >= target;
-// m_above returns the mass of the buckets above d.
-__device__ __forceinline__ void scan_first_digit(const double* mass, uint64_t target,
-                                                 uint32_t p_den, uint64_t& m_above, int& d_out) {
-  constexpr int PER = kH1 / 64;
-  const int lane = threadIdx.x & 63;
-  uint64_t mv[PER];
-  uint64_t lm = 0;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    mv[u] = (uint64_t)mass[lane * PER + u];
-    lm += mv[u];
-  }
-  uint64_t sm = lm;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t vm = shfl_down_u64(sm, off);
-    if (lane + off < 64) sm += vm;
-  }
-  uint64_t cum = sm - lm;  // mass of the buckets of higher lanes
-  int best = -1;
-  uint64_t best_m = 0;
-#pragma unroll
-  for (int u = PER - 1; u >= 0; --u) {
-    const uint64_t before = cum;
-    cum += mv[u];
-    if (best < 0 && cum * (uint64_t)p_den >= target) {
-      best = lane * PER + u;
-      best_m = before;
-    }
-  }
-  const unsigned long long ok = __ballot(best >= 0);
-  const int hl = 63 - __clzll(ok);
-  d_out = __shfl(best, hl);
-  const unsigned lo = __shfl((unsigned)best_m, hl), hi = __shfl((unsigned)(best_m >> 32), hl);
-  m_above = ((uint64_t)hi << 32) | lo;
-}
 
 struct DemandArgs {
   const uint16_t* k_pool;
@@ -289,6 +320,8 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
   __shared__ int s_dig[2];
   __shared__ uint64_t s_mab[2];
   __shared__ uint32_t s_cab[2];  // slots above the boundary so far, per view
+  __shared__ uint64_t s_wm[kDW];  // per-wave suffix totals of the digit searches
+  __shared__ uint32_t s_wc[kDW];
   if (!a.hdr->valid) return;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -589,36 +622,42 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     // loops are empty and its outputs are forced to 0 at the end); no branch
     // around this phase's barriers, so the row loop keeps one plain structure.
     {
-    // first digit of both views (waves 0 and 1), then one pass over the key
-    // ring collects each view's boundary-bucket members into its half of the
-    // LDS list and counts the slots in buckets above it
-    if (w < 2) {
-      uint64_t mab = 0;
-      int d1;
-      scan_first_digit(h1m + w * kH1, s_W[w] * (uint64_t)a.p_num, (uint32_t)a.p_den, mab, d1);
-      if (lane == 0) {
-        s_dig[w] = d1;
-        s_mab[w] = mab;
-        s_cab[w] = 0;
-        s_list_n[w] = 0;
-      }
+    // first digit of both views (the whole block searches), then one pass
+    // over the key ring collects each view's boundary-bucket members into its
+    // half of the LDS list and counts the slots in buckets above it
+    if (t < 2) {
+      s_cab[t] = 0;
+      s_list_n[t] = 0;
     }
+    block_first_digit(h1m, s_W, (uint32_t)a.p_num, (uint32_t)a.p_den, s_wm, s_dig, s_mab);
     __syncthreads();
     {
       const uint32_t d0 = (uint32_t)s_dig[0], d1 = (uint32_t)s_dig[1];
       uint32_t above0 = 0, above1 = 0;
-      for (int64_t i = t; i < ndem; i += kDT) {
-        const float2 kk = reinterpret_cast<const float2*>(rk)[i];
-        const uint32_t k0 = __float_as_uint(kk.x), k1 = __float_as_uint(kk.y);
-        above0 += (k0 >> 20) > d0;
-        above1 += (k1 >> 20) > d1;
-        if ((k0 >> 20) == d0) {
-          const int idx = atomicAdd(&s_list_n[0], 1);
-          if (idx < kListHalf) list[idx] = k0;
+      // kRingU ring loads in flight per thread before any is used
+      const float2* rk2 = reinterpret_cast<const float2*>(rk);
+      for (int64_t i0 = t; i0 < ndem; i0 += (int64_t)kRingU * kDT) {
+        float2 kk[kRingU];
+#pragma unroll
+        for (int u = 0; u < kRingU; ++u) {
+          const int64_t i = i0 + (int64_t)u * kDT;
+          kk[u] = rk2[i < ndem ? i : i0];
         }
-        if ((k1 >> 20) == d1) {
-          const int idx = atomicAdd(&s_list_n[1], 1);
-          if (idx < kListHalf) list[kListHalf + idx] = k1;
+#pragma unroll
+        for (int u = 0; u < kRingU; ++u) {
+          if (i0 + (int64_t)u * kDT < ndem) {
+            const uint32_t k0 = __float_as_uint(kk[u].x), k1 = __float_as_uint(kk[u].y);
+            above0 += (k0 >> 20) > d0;
+            above1 += (k1 >> 20) > d1;
+            if ((k0 >> 20) == d0) {
+              const int idx = atomicAdd(&s_list_n[0], 1);
+              if (idx < kListHalf) list[idx] = k0;
+            }
+            if ((k1 >> 20) == d1) {
+              const int idx = atomicAdd(&s_list_n[1], 1);
+              if (idx < kListHalf) list[kListHalf + idx] = k1;
+            }
+          }
         }
       }
       above0 = wave_sum_u32(above0);
@@ -631,7 +670,7 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     __syncthreads();
     // digits 2 (bits 19..10) and 3 (bits 9..0) over each view's boundary
     // members, both views in the same passes (each into its own counts and
-    // masses; waves 0 and 1 then scan one view each)
+    // masses, then one block-wide search for both)
     {
       const bool in_lds0 = s_list_n[0] <= kListHalf, in_lds1 = s_list_n[1] <= kListHalf;
       uint32_t prefix0 = (uint32_t)s_dig[0] << 20, prefix1 = (uint32_t)s_dig[1] << 20;
@@ -673,18 +712,8 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
           }
         }
         __syncthreads();
-        if (w < 2) {
-          uint64_t mab = s_mab[w];
-          uint32_t cab = s_cab[w];
-          int dd;
-          scan_desc<kH2>(h2c + w * kH2, h2m + w * kH2, s_W[w] * (uint64_t)a.p_num,
-                         (uint32_t)a.p_den, mab, cab, dd);
-          if (lane == 0) {
-            s_dig[w] = dd;
-            s_mab[w] = mab;
-            s_cab[w] = cab;
-          }
-        }
+        block_next_digit(h2c, h2m, s_W, (uint32_t)a.p_num, (uint32_t)a.p_den, s_wm, s_wc, s_dig,
+                         s_mab, s_cab);
         __syncthreads();
         prefix0 |= (uint32_t)s_dig[0] << shift;
         prefix1 |= (uint32_t)s_dig[1] << shift;
