@@ -30,6 +30,60 @@ constexpr int kMaxRowTokens = 65536;
 constexpr int kSelLdsTokens = 32768;  // candidates held in LDS (128 KiB)
 constexpr int kSelH1 = 2048;          // first radix digit: bits 30..20
 constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
+constexpr int kLoadU = 8;             // row loads in flight per thread
+static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per thread");
+
+// Inclusive prefix sums over a wave: lane L gets the sum over lanes 0..L.
+// DPP row shifts (lane i reads lane i - n of its 16-lane row, 0 before the
+// row's start) give the sums within each row; each row then adds the totals
+// of the rows below it, read from their last lanes.
+__device__ __forceinline__ uint32_t wave_prefix_u32(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                 r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
+// One radix pass's search over the whole block: thread t holds buckets
+// PER t .. PER t + PER - 1 of hcnt.  The digit is the smallest bucket whose
+// count of smaller values (below, plus the buckets up to and including it)
+// reaches nd; counts grow with the bucket, so one bucket has the crossing and
+// the thread holding it writes the extended prefix and the count below it.
+// (If no bucket reaches nd, the row has fewer than nd candidates; the top
+// bucket is taken and the caller reports the short row.)  Wave prefix sums
+// by DPP, one barrier for the totals of the lower waves.
+template <int PER>
+__device__ __forceinline__ void block_select_digit(const uint32_t* hcnt, uint32_t below, int nd,
+                                                   uint32_t prefix, int shift, uint32_t* s_wc,
+                                                   uint32_t& s_prefix, uint32_t& s_below) {
+  constexpr int nb = PER * kSel;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  uint32_t c[PER], own = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    c[u] = hcnt[PER * t + u];
+    own += c[u];
+  }
+  const uint32_t incl = wave_prefix_u32(own);
+  if (lane == 63) s_wc[wv] = incl;
+  __syncthreads();
+  uint32_t cum = below + (incl - own);
+  for (int u = 0; u < wv; ++u) cum += s_wc[u];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t before = cum;
+    cum += c[u];
+    const int bkt = PER * t + u;
+    if ((cum >= (uint32_t)nd && before < (uint32_t)nd) || (bkt == nb - 1 && cum < (uint32_t)nd)) {
+      s_prefix = prefix | ((uint32_t)bkt << shift);
+      s_below = before;
+    }
+  }
+}
 
 // Steps 2-3: the nd smallest candidates of [0, nc) (skipping those marked in
 // the S_loc bitmap when PROT), written ascending to dst (and dst2); without
@@ -57,35 +111,12 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
       if ((key & mask) == prefix) atomicAdd(&hcnt[(key >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    if (wv == 0) {
-      // ascending scan: the bucket where the count of smaller values reaches nd
-      const int per = nb / 64;
-      uint32_t lc = 0;
-      for (int u = 0; u < per; ++u) lc += hcnt[per * lane + u];
-      uint32_t incl = lc;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      uint32_t cum = below + incl - lc;
-      int best = -1;
-      uint32_t best_below = 0;
-      for (int u = 0; u < per; ++u) {
-        const uint32_t before = cum;
-        cum += hcnt[per * lane + u];
-        if (best < 0 && cum >= (uint32_t)nd) {
-          best = per * lane + u;
-          best_below = before;
-        }
-      }
-      const unsigned long long ok = __ballot(best >= 0);
-      const int ll = __ffsll((long long)ok) - 1;
-      if (lane == ll) {
-        s_prefix = prefix | ((uint32_t)best << shift);
-        s_below = best_below;
-      }
-    }
+    // the bucket where the count of smaller values reaches nd
+    uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
+    if (pass == 0)
+      block_select_digit<kSelH1 / kSel>(hcnt, below, nd, prefix, shift, s_wc, s_prefix, s_below);
+    else
+      block_select_digit<kSelH2 / kSel>(hcnt, below, nd, prefix, shift, s_wc, s_prefix, s_below);
     __syncthreads();
     prefix = s_prefix;
     below = s_below;
@@ -296,9 +327,17 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   const int nd = m * b;  // candidates to drop
   if (nc <= kSelLdsTokens) {
     // the row's candidates are read from HBM once, every pass runs on LDS
+    // (kLoadU loads in flight per thread before any is stored)
     const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
-    for (int i = t; i < n4; i += kSel)
-      reinterpret_cast<float4*>(srow)[i] = reinterpret_cast<const float4*>(s)[i];
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    for (int i0 = t; i0 < n4; i0 += kLoadU * kSel) {
+      float4 v[kLoadU];
+#pragma unroll
+      for (int u = 0; u < kLoadU; ++u) v[u] = s4[i0 + u * kSel < n4 ? i0 + u * kSel : i0];
+#pragma unroll
+      for (int u = 0; u < kLoadU; ++u)
+        if (i0 + u * kSel < n4) reinterpret_cast<float4*>(srow)[i0 + u * kSel] = v[u];
+    }
     __syncthreads();
     select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
                dst2, err);
