@@ -324,8 +324,9 @@ gp_status gp_decode_attention_static(gp_ctx* ctx, const gp_pool* pool, const gp_
 /* Kernels of the event, for gp_profile_read. */
 enum gp_kernel_id {
   GP_K_EMA = 0,     /* A0 summary update */
-  GP_K_PLAN = 1,    /* batch prefix sums, work order and validation */
-  GP_K_QHAT = 2,    /* A1 calibrate + rotate */
+  GP_K_PLAN = 1,    /* batch prefix sums, work order and validation: runs inside the
+                       GP_K_QHAT launch, so it records no launches of its own */
+  GP_K_QHAT = 2,    /* A1 calibrate + rotate, with the batch plan in the same launch */
   GP_K_DEMAND = 3,  /* A2-A4 paged key scoring, distributions, importance, D_p */
   GP_K_DECIDE = 4,  /* A5 trend and decision */
   GP_K_GROW = 5,    /* A6 page grant and fallback */

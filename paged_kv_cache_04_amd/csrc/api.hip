@@ -244,15 +244,11 @@ gp_status gp_demand(gp_ctx* c, const gp_pool* pool, const gp_batch* bt, const fl
   const gp::WsLayout w = gp::ws_layout(c->p, B, total_tokens, max_tokens, c->num_cus * gp::kDemandBlocksPerCU);
   if (!ws || ws_bytes < w.total) return GP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = timed(c, GP_K_PLAN, s, [&] {
-    return gp::launch_plan(c->p, w, bt->num_pages, B, bt->max_pages, total_pages, ws, c->d_err,
-                           s);
+  // the plan runs inside the summaries launch (its own block)
+  hipError_t e = timed(c, GP_K_QHAT, s, [&] {
+    return gp::launch_prep(c->p, w, qstate, q_cur, rope, rope_rows, bt->slot, bt->position,
+                           bt->num_pages, B, bt->max_pages, total_pages, ws, c->d_err, s);
   });
-  if (e == hipSuccess)
-    e = timed(c, GP_K_QHAT, s, [&] {
-      return gp::launch_qhat(c->p, w, qstate, q_cur, rope, rope_rows, bt->slot, bt->position, B,
-                             ws, c->d_err, s);
-    });
   if (e == hipSuccess)
     e = timed(c, GP_K_DEMAND, s, [&] {
       return gp::launch_demand(c->p, w, pool->k_pool, pool->num_pages, bt->block_table,

@@ -133,6 +133,41 @@ __device__ __forceinline__ float gp_exp(float x) {
   return n < -100.0f ? 0.0f : y;
 }
 
+// Inclusive prefix sums over a wave: lane L gets the sum over lanes 0..L.
+// DPP row shifts (lane i reads lane i - n of its 16-lane row, 0 before the
+// row's start) give the sums within each row; each row then adds the totals
+// of the rows below it, read from their last lanes.
+__device__ __forceinline__ uint32_t wave_prefix_u32(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                 r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
+// Exclusive prefix sums over a block of nw waves (nw <= 16): returns the
+// sum of v over the threads before this one and, through total, the sum over
+// the block.  Ends with the block synchronised (s_w may be reused after).
+__device__ __forceinline__ uint32_t block_prefix_excl_u32(uint32_t v, uint32_t* s_w, int nw,
+                                                          uint32_t& total) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const uint32_t incl = wave_prefix_u32(v);
+  if (lane == 63) s_w[wv] = incl;
+  __syncthreads();
+  uint32_t before = incl - v, all = 0;
+  for (int u = 0; u < nw; ++u) {
+    const uint32_t x = s_w[u];
+    if (u < wv) before += x;
+    all += x;
+  }
+  total = all;
+  __syncthreads();
+  return before;
+}
+
 // Mass of a probability in 2^-40 units (exact: v * 2^40 <= 2^40).
 __device__ __forceinline__ uint64_t fix40(float v) { return (uint64_t)(v * kFix); }
 
@@ -141,13 +176,12 @@ __device__ __forceinline__ uint64_t fix40(float v) { return (uint64_t)(v * kFix)
 hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int32_t* slot,
                       const uint8_t* first, int B, int32_t* err, hipStream_t s);
 
-hipError_t launch_plan(const Params& p, const WsLayout& w, const int32_t* num_pages_dev, int B,
+// Rotated summaries (A1) and the batch plan, one launch.
+hipError_t launch_prep(const Params& p, const WsLayout& w, const float* qstate, const float* qcur,
+                       const float* rope, int rope_rows, const int32_t* slot,
+                       const int32_t* position, const int32_t* num_pages_dev, int B,
                        int max_pages, int64_t host_total_pages, void* ws, int32_t* err,
                        hipStream_t s);
-
-hipError_t launch_qhat(const Params& p, const WsLayout& w, const float* qstate, const float* qcur,
-                       const float* rope, int rope_rows, const int32_t* slot,
-                       const int32_t* position, int B, void* ws, int32_t* err, hipStream_t s);
 
 hipError_t launch_demand(const Params& p, const WsLayout& w, const uint16_t* k_pool,
                          int pool_pages, const int32_t* block_table, int max_pages, int B,

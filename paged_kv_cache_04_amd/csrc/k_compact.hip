@@ -66,15 +66,17 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
   // value that steers a branch is workgroup-uniform and read into a scalar
   auto item = [&](int r, int lh, int which) {
     const int row = r * LH + lh;
+    // the request's metadata in one round of loads
     const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+    const int P = __builtin_amdgcn_readfirstlane((int)(page_off[r + 1] - page_off[r]));
+    const int32_t flags = __builtin_amdgcn_readfirstlane(req_flags[r]);
     if (act != GP_COMPRESS && act != GP_SHRINK) return;
     if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
     const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots freed
     const int nd = m * b;                    // dropped slots
-    const int P = __builtin_amdgcn_readfirstlane((int)(page_off[r + 1] - page_off[r]));
     if (P < m + 1) return;
     // pages short (App. E.2), or longer than the selection takes
-    if (__builtin_amdgcn_readfirstlane(req_flags[r]) & (kReqBlocked | kReqTooLong)) return;
+    if (flags & (kReqBlocked | kReqTooLong)) return;
     const int l = lh / Hkv, h = lh % Hkv;
     if (t == 0) {
       bad = 0;

@@ -22,11 +22,16 @@ __global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau, int p
                                                 double* __restrict__ delta,
                                                 int8_t* __restrict__ decision) {
   __shared__ int64_t red[4];
-  if (!hdr->valid) return;
   const int r = blockIdx.x, t = threadIdx.x;
+  // every load is issued before the batch's validity is looked at (all of
+  // them lie inside the outputs of a valid launch; a rejected batch returns
+  // before any value is used)
+  const int valid = hdr->valid;
+  const int64_t off0 = page_off[r], off1 = page_off[r + 1];
   int64_t s = 0;
   for (int i = t; i < LH; i += 256)
     s += (int64_t)k_short[(int64_t)r * LH + i] - (int64_t)k_long[(int64_t)r * LH + i];
+  if (!valid) return;
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) {
     const unsigned lo = __shfl_xor((unsigned)(uint64_t)s, m);
@@ -37,7 +42,7 @@ __global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau, int p
   __syncthreads();
   if (t == 0) {
     const int64_t diff = red[0] + red[1] + red[2] + red[3];
-    const int64_t P = page_off[r + 1] - page_off[r];
+    const int64_t P = off1 - off0;
     const int64_t card = (P - 1) * b;
     double dl = 0.0;
     int grow = 1;
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
                                                     int32_t* __restrict__ refcount,
                                                     int64_t* __restrict__ counters,
                                                     int32_t* __restrict__ err) {
-  __shared__ int scan[kMaxBatch];
+  __shared__ uint32_t s_w[kMaxBatch / 64];
   __shared__ int n_fallback, n_shrink;
   const int t = threadIdx.x;
   if (t == 0) n_fallback = n_shrink = 0;
@@ -112,16 +117,9 @@ __global__ __launch_bounds__(kMaxBatch) void k_grow(int B, int max_pages, int po
     P = num_pages[t];
     want = dec_grow && P >= 1 && P < max_pages;
   }
-  scan[t] = want ? 1 : 0;
-  __syncthreads();
-  for (int off = 1; off < kMaxBatch; off <<= 1) {
-    const int add = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  const int rank = scan[t] - (want ? 1 : 0);  // exclusive
-  const int total_want = scan[kMaxBatch - 1];
+  uint32_t total_u = 0;
+  const int rank = (int)block_prefix_excl_u32(want ? 1u : 0u, s_w, kMaxBatch / 64, total_u);
+  const int total_want = (int)total_u;
   const bool granted = want && rank < avail;
   if (t < B) {
     if (granted) {

@@ -33,21 +33,6 @@ constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
 constexpr int kLoadU = 8;             // row loads in flight per thread
 static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per thread");
 
-// Inclusive prefix sums over a wave: lane L gets the sum over lanes 0..L.
-// DPP row shifts (lane i reads lane i - n of its 16-lane row, 0 before the
-// row's start) give the sums within each row; each row then adds the totals
-// of the rows below it, read from their last lanes.
-__device__ __forceinline__ uint32_t wave_prefix_u32(uint32_t v) {
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);
-  const int row = (threadIdx.x & 63) >> 4;
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-                 r2 = __builtin_amdgcn_readlane(v, 47);
-  return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
-}
-
 // One radix pass's search over the whole block: thread t holds buckets
 // PER t .. PER t + PER - 1 of hcnt.  The digit is the smallest bucket whose
 // count of smaller values (below, plus the buckets up to and including it)
@@ -300,17 +285,22 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   __shared__ int scanbuf[2 * (kSel / 64)];
   __shared__ int blkcnt[kMaxRowTokens / kPage];
   __shared__ uint32_t s_prefix, s_below;
-  if (!hdr->valid) return;
   const int LH = L * Hkv;
   const int row = blockIdx.x;
   const int r = row / LH, lh = row % LH;
+  // the row's metadata in one round of loads (all inside the workspace and
+  // the caller's arrays whatever the batch), looked at after validity
+  const int valid = hdr->valid;
   const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+  const int64_t off0 = page_off[r], off1 = page_off[r + 1];
+  const int32_t flags = req_flags[r];
+  if (!valid) return;
   if (act != GP_COMPRESS && act != GP_SHRINK) return;
   if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
   const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
-  const int64_t P = page_off[r + 1] - page_off[r];
+  const int64_t P = off1 - off0;
   const int t = threadIdx.x;
-  if (req_flags[r] & kReqTooLong) {  // longer than the selection takes: left as it is
+  if (flags & kReqTooLong) {  // longer than the selection takes: left as it is
     if (t == 0 && lh == 0) atomicOr(err, GP_DEVERR_LONG);
     return;
   }
@@ -318,9 +308,9 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
     if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
     return;
   }
-  if (req_flags[r] & kReqBlocked) return;  // left uncompressed (App. E.2 page shortage)
+  if (flags & kReqBlocked) return;  // left uncompressed (App. E.2 page shortage)
   const int N = (int)(P * b), nc = N - R;
-  const int64_t row_tok = (int64_t)LH * page_off[r] * b + (int64_t)lh * N;
+  const int64_t row_tok = (int64_t)LH * off0 * b + (int64_t)lh * N;
   const float* __restrict__ s = imp + row_tok;
   int32_t* dst = dropped + (int64_t)row * stride;
   int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;

@@ -74,46 +74,56 @@ hipError_t launch_ema(const Params& p, float* qstate, const float* q, const int3
 // request is longer than the workspace's per-row rings and the total equals
 // the host's; every later kernel of the event exits at once on a rejected
 // batch, so a stale host mirror can never send a kernel outside the workspace.
+// Runs as the last block of the summaries launch below.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_pages, int B,
-                                               int max_pages, int64_t host_total_pages, int b,
-                                               int64_t ring_tokens, WsHeader* __restrict__ hdr,
-                                               int64_t* __restrict__ page_off,
-                                               int32_t* __restrict__ req_order,
-                                               int32_t* __restrict__ req_flags,
-                                               int32_t* __restrict__ err) {
-  __shared__ int64_t buf[kMaxBatch];
+constexpr int kPrepT = 256;                  // threads per block of the launch
+constexpr int kPlanPer = kMaxBatch / kPrepT;  // requests per thread of the plan block
+
+__device__ __forceinline__ void plan_block(const int32_t* __restrict__ num_pages, int B,
+                                           int max_pages, int64_t host_total_pages, int b,
+                                           int64_t ring_tokens, WsHeader* __restrict__ hdr,
+                                           int64_t* __restrict__ page_off,
+                                           int32_t* __restrict__ req_order,
+                                           int32_t* __restrict__ req_flags,
+                                           int32_t* __restrict__ err) {
   __shared__ int32_t pages[kMaxBatch];
-  __shared__ int bad;
+  __shared__ uint32_t s_w[kPrepT / 64];
   const int t = threadIdx.x;
-  if (t == 0) bad = 0;
-  __syncthreads();
-  int64_t v = 0;
-  if (t < B) {
-    const int P = num_pages[t];
-    if (P < 1 || P > max_pages || (int64_t)P * b > ring_tokens) atomicOr(&bad, 1);
-    v = P;
-    pages[t] = P;
+  // thread t takes requests kPlanPer t .. kPlanPer t + kPlanPer - 1
+  int P[kPlanPer];
+  bool any_bad = false;
+  uint32_t v[kPlanPer], mine = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanPer; ++k) {
+    const int r = kPlanPer * t + k;
+    P[k] = r < B ? num_pages[r] : 0;
+    const bool ok_p = P[k] >= 1 && P[k] <= max_pages && (int64_t)P[k] * b <= ring_tokens;
+    any_bad |= r < B && !ok_p;
+    // counts outside [1, max_pages] reject the batch; they enter the sums as
+    // 0 so the 32-bit prefix cannot wrap (valid counts sum to at most
+    // 1024 * max_pages)
+    v[k] = (r < B && ok_p) ? (uint32_t)P[k] : 0u;
+    mine += v[k];
+    if (r < B) pages[r] = P[k];
   }
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kMaxBatch; off <<= 1) {
-    const int64_t add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
-  }
-  if (t < B) {
-    req_flags[t] = (int64_t)pages[t] * b > kMaxCompressTokens ? kReqTooLong : 0;
-    page_off[t + 1] = buf[t];
-    const int32_t mine = pages[t];
-    int rank = 0;
-    for (int u = 0; u < B; ++u) rank += (pages[u] > mine) || (pages[u] == mine && u < t);
-    req_order[rank] = t;
+  const int bad = __syncthreads_or(any_bad);
+  uint32_t total_u = 0;
+  uint32_t before = block_prefix_excl_u32(mine, s_w, kPrepT / 64, total_u);
+#pragma unroll
+  for (int k = 0; k < kPlanPer; ++k) {
+    const int r = kPlanPer * t + k;
+    before += v[k];
+    if (r < B) {
+      req_flags[r] = (int64_t)P[k] * b > kMaxCompressTokens ? kReqTooLong : 0;
+      page_off[r + 1] = (int64_t)before;
+      int rank = 0;
+      for (int u = 0; u < B; ++u) rank += (pages[u] > P[k]) || (pages[u] == P[k] && u < r);
+      req_order[rank] = r;
+    }
   }
   if (t == 0) {
     page_off[0] = 0;
-    const int64_t total = buf[B - 1];
+    const int64_t total = (int64_t)total_u;
     const int ok = (!bad) && total == host_total_pages;
     hdr->magic = kWsMagic;
     hdr->batch = B;
@@ -124,23 +134,10 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ num_p
   }
 }
 
-hipError_t launch_plan(const Params& p, const WsLayout& w, const int32_t* num_pages_dev, int B,
-                       int max_pages, int64_t host_total_pages, void* ws, int32_t* err,
-                       hipStream_t s) {
-  char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kMaxBatch), 0, s, num_pages_dev, B, max_pages,
-                     host_total_pages, p.b, w.ring_tokens,
-                     reinterpret_cast<WsHeader*>(base + w.header),
-                     reinterpret_cast<int64_t*>(base + w.page_off),
-                     reinterpret_cast<int32_t*>(base + w.req_order),
-                     reinterpret_cast<int32_t*>(base + w.req_flags), err);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // A1: calibrated, rotated summaries (App. E.1 Eq. 12 and the paragraph after
-// it).  One block per (request, layer); thread x*Hq + hq handles summary x of
-// query head hq:
+// it), one (request, layer) pair per block; thread x*Hq + hq handles
+// summary x of query head hq:
 //   gamma = sqrt(ss(q_t) / ss(qbar)) (serial fmaf sums of squares; 0 when
 //   ss(qbar) = 0), qtilde = gamma * qbar, rotate-half rotary at the current
 //   position with the caller's (cos, sin) row, times 1/sqrt(d).
@@ -148,42 +145,38 @@ hipError_t launch_plan(const Params& p, const WsLayout& w, const int32_t* num_pa
 // query index x * 4 + g for the g-th query head of the KV head (GQA grouping
 // of consecutive query heads); element j sits in quad j / 4 at j % 4, so the
 // scoring kernel reads the 32 values of one 4-element key quad contiguously.
+// It reads no page count, so it runs beside the plan in the same launch (a
+// rejected batch stops at the demand kernel).  Loads that do not depend on
+// each other are issued together: the current query with the slot and
+// position, then the summaries (the rotary row follows, in the rotation).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_qhat(const float* __restrict__ qstate,
-                                              const float* __restrict__ qcur,
-                                              const float* __restrict__ rope, int rope_rows,
-                                              const int32_t* __restrict__ slot,
-                                              const int32_t* __restrict__ position, int L, int M,
-                                              int Hq, int Hkv, const WsHeader* __restrict__ hdr,
-                                              float* __restrict__ qhat, int32_t* __restrict__ err) {
-  if (!hdr->valid) return;
-  const int r = blockIdx.x / L, l = blockIdx.x % L;
-  const int t = threadIdx.x;
-  if (t >= 2 * Hq) return;
-  const int x = t / Hq, hq = t % Hq;
-  int s = slot[r];
-  bool zero = false;
-  if (s < 0 || s >= M) {
-    if (t == 0) atomicOr(err, GP_DEVERR_SLOT);
-    zero = true;
-    s = 0;
-  }
-  int pos = position[r];
-  if (pos < 0 || pos >= rope_rows) {
-    if (t == 0) atomicOr(err, GP_DEVERR_POSITION);
-    pos = pos < 0 ? 0 : rope_rows - 1;
-  }
-  // both vectors are read with 16-byte loads, all issued before the serial
-  // sums of squares run over them in index order
+__device__ __forceinline__ void qhat_slice(int pair, int tt, const float* __restrict__ qstate,
+                                           const float* __restrict__ qcur,
+                                           const float* __restrict__ rope, int rope_rows,
+                                           const int32_t* __restrict__ slot,
+                                           const int32_t* __restrict__ position, int L, int M,
+                                           int Hq, int Hkv, float* __restrict__ qhat,
+                                           int32_t* __restrict__ err) {
+  const int r = pair / L, l = pair % L;
+  const int x = tt / Hq, hq = tt % Hq;
+  const int s_raw = slot[r], pos_raw = position[r];
   const float4* qt = reinterpret_cast<const float4*>(qcur + (((int64_t)r * L + l) * Hq + hq) * kD);
+  float4 tv[kD / 4];
+#pragma unroll
+  for (int i = 0; i < kD / 4; ++i) tv[i] = qt[i];
+  const bool zero = s_raw < 0 || s_raw >= M;
+  if (zero && tt == 0) atomicOr(err, GP_DEVERR_SLOT);
+  const int s = zero ? 0 : s_raw;
+  const bool pos_bad = pos_raw < 0 || pos_raw >= rope_rows;
+  if (pos_bad && tt == 0) atomicOr(err, GP_DEVERR_POSITION);
+  const int pos = pos_raw < 0 ? 0 : (pos_raw >= rope_rows ? rope_rows - 1 : pos_raw);
   const float4* qb =
       reinterpret_cast<const float4*>(qstate + ((((int64_t)l * M + s) * 2 + x) * Hq + hq) * kD);
-  float4 tv[kD / 4], bv[kD / 4];
+  const float4* cs = reinterpret_cast<const float4*>(rope + (int64_t)pos * kD);
+  constexpr int hq4 = kD / 8;  // quads per half
+  float4 bv[kD / 4];
 #pragma unroll
-  for (int i = 0; i < kD / 4; ++i) {
-    tv[i] = qt[i];
-    bv[i] = qb[i];
-  }
+  for (int i = 0; i < kD / 4; ++i) bv[i] = qb[i];
   float ssq = 0.0f, ssx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kD / 4; ++i) {
@@ -202,11 +195,9 @@ __global__ __launch_bounds__(256) void k_qhat(const float* __restrict__ qstate,
   float gamma = ssx > 0.0f ? __builtin_sqrtf(ssq / ssx) : 0.0f;
   if (zero) gamma = 0.0f;
   const float scale = 1.0f / __builtin_sqrtf((float)kD);
-  const float4* cs = reinterpret_cast<const float4*>(rope + (int64_t)pos * kD);
   const int kvh = hq / kGroup, qi = x * kGroup + hq % kGroup;
   float* out = qhat + (((int64_t)r * L + l) * Hkv + kvh) * (kNQ * kD);
   // element j of the first half pairs with j + d/2; quad i holds j = 4i .. 4i+3
-  constexpr int hq4 = kD / 8;  // quads per half
   auto rot = [&](float b1, float b2, float c, float sn, float& y1, float& y2) {
     const float a = gamma * b1, c2 = gamma * b2;
     y1 = __builtin_fmaf(a, c, -(c2 * sn)) * scale;
@@ -225,14 +216,42 @@ __global__ __launch_bounds__(256) void k_qhat(const float* __restrict__ qstate,
   }
 }
 
-hipError_t launch_qhat(const Params& p, const WsLayout& w, const float* qstate, const float* qcur,
+// The summaries launch: block p < B L computes the rotated summaries of
+// (request, layer) pair p, block B L runs the plan.
+__global__ __launch_bounds__(kPrepT) void k_prep(
+    const float* __restrict__ qstate, const float* __restrict__ qcur,
+    const float* __restrict__ rope, int rope_rows, const int32_t* __restrict__ slot,
+    const int32_t* __restrict__ position, int L, int M, int Hq, int Hkv,
+    float* __restrict__ qhat, const int32_t* __restrict__ num_pages, int B, int max_pages,
+    int64_t host_total_pages, int b, int64_t ring_tokens, WsHeader* __restrict__ hdr,
+    int64_t* __restrict__ page_off, int32_t* __restrict__ req_order,
+    int32_t* __restrict__ req_flags, int32_t* __restrict__ err) {
+  if ((int)blockIdx.x == B * L) {
+    plan_block(num_pages, B, max_pages, host_total_pages, b, ring_tokens, hdr, page_off,
+               req_order, req_flags, err);
+    return;
+  }
+  const int t = threadIdx.x;
+  if (t >= 2 * Hq) return;
+  qhat_slice((int)blockIdx.x, t, qstate, qcur, rope, rope_rows, slot, position, L, M, Hq, Hkv,
+             qhat, err);
+}
+
+hipError_t launch_prep(const Params& p, const WsLayout& w, const float* qstate, const float* qcur,
                        const float* rope, int rope_rows, const int32_t* slot,
-                       const int32_t* position, int B, void* ws, int32_t* err, hipStream_t s) {
+                       const int32_t* position, const int32_t* num_pages_dev, int B,
+                       int max_pages, int64_t host_total_pages, void* ws, int32_t* err,
+                       hipStream_t s) {
+  if (2 * p.Hq > kPrepT) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(k_qhat, dim3((unsigned)(B * p.L)), dim3(256), 0, s, qstate, qcur, rope,
-                     rope_rows, slot, position, p.L, p.M, p.Hq, p.Hkv,
-                     reinterpret_cast<const WsHeader*>(base + w.header),
-                     reinterpret_cast<float*>(base + w.qhat), err);
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)(B * p.L + 1)), dim3(kPrepT), 0, s, qstate, qcur,
+                     rope, rope_rows, slot, position, p.L, p.M, p.Hq, p.Hkv,
+                     reinterpret_cast<float*>(base + w.qhat), num_pages_dev, B, max_pages,
+                     host_total_pages, p.b, w.ring_tokens,
+                     reinterpret_cast<WsHeader*>(base + w.header),
+                     reinterpret_cast<int64_t*>(base + w.page_off),
+                     reinterpret_cast<int32_t*>(base + w.req_order),
+                     reinterpret_cast<int32_t*>(base + w.req_flags), err);
   return hipGetLastError();
 }
 
