@@ -2,7 +2,8 @@
 
 Flags: fp32 arithmetic exactly as written (no FMA contraction beyond explicit
 fmaf, correctly rounded division and square root, denormals kept), packed
-fp32 instructions disabled, one shared library for all kernels and the C ABI.
+fp32 instructions disabled, one shared library for all kernels and the C ABI,
+linked with no undefined symbols.
 """
 import glob
 import os
@@ -20,6 +21,9 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    # every symbol resolved at link time: a missing kernel launcher fails the
+    # build instead of the first call
+    "-Wl,--no-undefined",
 ]
 
 
