@@ -98,6 +98,33 @@ def test_stale_host_page_counts():
 
 
 @needs_gpu
+@pytest.mark.parametrize("dev_pages", [(0, 7), (5, 2)])
+def test_device_page_counts_outside_limits(dev_pages):
+    """Device page counts whose total agrees with the host mirror but which
+    break a limit: a count of 0, or a count longer than the workspace's
+    per-row rings (sized from the host mirror's longest request, 4 pages).
+    The plan rejects the batch, PAGES is raised, and no later kernel of the
+    event touches the outputs or the pool."""
+    log(f"test_device_page_counts_outside_limits {dev_pages}")
+    wl = _workload(44)
+    cfg = gb_config(wl.shape, max_slots=wl.max_slots)
+    run = runner_for(wl, cfg)
+    q = run_stream_gpu(run, wl)
+    assert list(run.batch.num_pages_host) == [4, 3]
+    wl.num_pages.copy_(torch.tensor(dev_pages, dtype=torch.int32, device="cuda"))
+    run.out.k_short.fill_(-7)
+    pages = wl.block_table[1, :3].cpu().numpy().copy()
+    k_before = device_rows(wl.k_pool, 0, 0, pages)
+    run.demand(q)
+    run.grow(decision=torch.zeros(2, dtype=torch.int8, device="cuda"))
+    run.compress()
+    torch.cuda.synchronize()
+    assert run.device_errors() & ERR_PAGES
+    assert (run.out.k_short == -7).all()
+    assert np.array_equal(device_rows(wl.k_pool, 0, 0, pages), k_before)
+
+
+@needs_gpu
 def test_host_validation_errors():
     """Calls that host-side validation refuses return an error status and
     enqueue nothing: a workspace smaller than gp_workspace_bytes, Compress &
