@@ -32,12 +32,7 @@ __global__ __launch_bounds__(256) void k_decide(int LH, int b, double tau, int p
   for (int i = t; i < LH; i += 256)
     s += (int64_t)k_short[(int64_t)r * LH + i] - (int64_t)k_long[(int64_t)r * LH + i];
   if (!valid) return;
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) {
-    const unsigned lo = __shfl_xor((unsigned)(uint64_t)s, m);
-    const unsigned hi = __shfl_xor((unsigned)((uint64_t)s >> 32), m);
-    s += (int64_t)(((uint64_t)hi << 32) | lo);
-  }
+  s = (int64_t)wave_sum_u64((uint64_t)s);  // two's complement: the wrap-around sum is exact
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
   if (t == 0) {

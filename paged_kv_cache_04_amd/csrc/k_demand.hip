@@ -77,55 +77,6 @@ __device__ __forceinline__ uint64_t shfl_down_u64(uint64_t v, int off) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Cross-lane sums without LDS traffic: DPP rotations within each 16-lane
-// row, and gfx950's permlane swaps, which exchange the odd 16-lane rows of
-// one register with the even rows of another (permlane16) or the upper 32
-// lanes of one with the lower 32 of another (permlane32).
-__device__ __forceinline__ uint64_t pk64(uint32_t lo, uint32_t hi) {
-  return ((uint64_t)hi << 32) | lo;
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
-  return pk64(lo, hi);
-}
-
-// sum over the 16 lanes of each row, in every lane of the row (row_ror 8, 4, 2, 1)
-__device__ __forceinline__ uint64_t row_sum_u64(uint64_t v) {
-  v += dpp_u64<0x128>(v);
-  v += dpp_u64<0x124>(v);
-  v += dpp_u64<0x122>(v);
-  v += dpp_u64<0x121>(v);
-  return v;
-}
-
-// a + b after lanes 32..63 of a trade places with lanes 0..31 of b: lanes
-// 0..31 get a's value there plus a's value 32 lanes up, lanes 32..63 b's
-// value plus b's value 32 lanes down
-__device__ __forceinline__ uint64_t swap32_add(uint64_t a, uint64_t b) {
-  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)b, false, false);
-  const auto hi =
-      __builtin_amdgcn_permlane32_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
-  return pk64(lo[0], hi[0]) + pk64(lo[1], hi[1]);
-}
-
-// the same with the odd 16-lane rows of a and the even rows of b
-__device__ __forceinline__ uint64_t swap16_add(uint64_t a, uint64_t b) {
-  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)b, false, false);
-  const auto hi =
-      __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
-  return pk64(lo[0], hi[0]) + pk64(lo[1], hi[1]);
-}
-
-// sum over the wave, in every lane
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-  v = row_sum_u64(v);
-  v = swap16_add(v, v);
-  return swap32_add(v, v);
-}
-
 // 16 values per lane summed over the wave, transposed: each exchange halves
 // the values a lane carries.  Lane L ends with the totals of values
 // 8 b5 + 4 b4 + j (j = 0..3) in out[j], b5 and b4 being bits 5 and 4 of L.
@@ -263,16 +214,6 @@ __device__ __forceinline__ float uniform_f(float v) {
 // is exact and from 2^23 on every fp32 value is an integer (v <= 1).
 __device__ __forceinline__ float mass40(float v) { return __builtin_floorf(v * kFix); }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x124, 0xf, 0xf, false);
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x122, 0xf, 0xf, false);
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x121, 0xf, 0xf, false);
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = a[0] + a[1];
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return b[0] + b[1];
-}
 
 // The logits ring holds, per 64-key tile, the first four logits of its keys
 // and then the last four ([tile][2][64][4] floats), so that each store

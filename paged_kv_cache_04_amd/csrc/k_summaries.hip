@@ -148,7 +148,7 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ num_pages
 // It reads no page count, so it runs beside the plan in the same launch (a
 // rejected batch stops at the demand kernel).  Loads that do not depend on
 // each other are issued together: the current query with the slot and
-// position, then the summaries (the rotary row follows, in the rotation).
+// position, then the summaries with the rotary row.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void qhat_slice(int pair, int tt, const float* __restrict__ qstate,
                                            const float* __restrict__ qcur,
@@ -174,9 +174,12 @@ __device__ __forceinline__ void qhat_slice(int pair, int tt, const float* __rest
       reinterpret_cast<const float4*>(qstate + ((((int64_t)l * M + s) * 2 + x) * Hq + hq) * kD);
   const float4* cs = reinterpret_cast<const float4*>(rope + (int64_t)pos * kD);
   constexpr int hq4 = kD / 8;  // quads per half
-  float4 bv[kD / 4];
+  float4 bv[kD / 4], cv[kD / 4];
 #pragma unroll
-  for (int i = 0; i < kD / 4; ++i) bv[i] = qb[i];
+  for (int i = 0; i < kD / 4; ++i) {
+    bv[i] = qb[i];
+    cv[i] = cs[i];
+  }
   float ssq = 0.0f, ssx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kD / 4; ++i) {
@@ -205,7 +208,7 @@ __device__ __forceinline__ void qhat_slice(int pair, int tt, const float* __rest
   };
 #pragma unroll
   for (int i = 0; i < hq4; ++i) {
-    const float4 c = cs[i], sn = cs[hq4 + i], b1 = bv[i], b2 = bv[hq4 + i];
+    const float4 c = cv[i], sn = cv[hq4 + i], b1 = bv[i], b2 = bv[hq4 + i];
     float4 y1, y2;
     rot(b1.x, b2.x, c.x, sn.x, y1.x, y2.x);
     rot(b1.y, b2.y, c.y, sn.y, y1.y, y2.y);
