@@ -226,6 +226,17 @@ __device__ __forceinline__ void load_logits8(const float* lg, int64_t i, float (
 }
 
 
+// Compile-time tags for the token loops of phases 2 and 3: when every
+// query's maximum over C_t equals its maximum over all slots (the usual
+// case) the demand and full-cache exponentials coincide and the loop body is
+// one block of 8 independent exponentials, with no per-query branch.
+struct AllSame {
+  static constexpr bool value = true;
+};
+struct SomeDiffer {
+  static constexpr bool value = false;
+};
+
 struct DemandArgs {
   const uint16_t* k_pool;
   int pool_pages;
@@ -435,11 +446,13 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     __syncthreads();
     float mdem[kNQ], mall[kNQ];
     bool same[kNQ];
+    bool all_same = true;
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) {  // block-uniform: held in scalar registers
       mdem[q] = uniform_f(s_m[0][q]);
       mall[q] = uniform_f(s_m[1][q]);
       same[q] = mdem[q] == mall[q];
+      all_same = all_same && same[q];
     }
 
     // ---- 2. exact fixed-point normalisers ----------------------------------------
@@ -452,15 +465,22 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
       double zc[kNQ], zd[kNQ];
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) zc[q] = zd[q] = 0.0;
-      for (int64_t i = t; i < ndem; i += kDT) {
-        float lv[kNQ];
-        load_logits8(lg, i, lv);
+      auto ct_terms = [&](auto tag) {
+        for (int64_t i = t; i < ndem; i += kDT) {
+          float lv[kNQ];
+          load_logits8(lg, i, lv);
 #pragma unroll
-        for (int q = 0; q < kNQ; ++q) {
-          zc[q] += (double)mass40(gp_exp(lv[q] - mall[q]));
-          if (!same[q]) zd[q] += (double)mass40(gp_exp(lv[q] - mdem[q]));
+          for (int q = 0; q < kNQ; ++q) {
+            zc[q] += (double)mass40(gp_exp(lv[q] - mall[q]));
+            if (!decltype(tag)::value && !same[q])
+              zd[q] += (double)mass40(gp_exp(lv[q] - mdem[q]));
+          }
         }
-      }
+      };
+      if (all_same)
+        ct_terms(AllSame{});
+      else
+        ct_terms(SomeDiffer{});
 #pragma unroll
       for (int q = 0; q < kNQ; ++q)
         if (same[q]) zd[q] = zc[q];
@@ -500,6 +520,7 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
         ra[q] = uniform_f(s_rho[1][q]);
       }
       double w0 = 0.0, w1 = 0.0;
+      auto ct_tokens = [&](auto tag) {
       for (int64_t i = t; i < ndem; i += kDT) {
         float lv[kNQ];
         load_logits8(lg, i, lv);
@@ -512,7 +533,7 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
             const int q = x * kGroup + g;
             const float ea = gp_exp(lv[q] - mall[q]);
             sa = sa + ea * ra[q];
-            const float ed = same[q] ? ea : gp_exp(lv[q] - mdem[q]);
+            const float ed = (decltype(tag)::value || same[q]) ? ea : gp_exp(lv[q] - mdem[q]);
             sd = sd + ed * rd[q];
           }
           aa[x] = sa * (1.0f / (float)kGroup);
@@ -527,6 +548,11 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
         w0 += (double)f0;
         w1 += (double)f1;
       }
+      };
+      if (all_same)
+        ct_tokens(AllSame{});
+      else
+        ct_tokens(SomeDiffer{});
       for (int64_t i = ndem + t; i < N; i += kDT) {
         float lv[kNQ];
         load_logits8(lg, i, lv);
