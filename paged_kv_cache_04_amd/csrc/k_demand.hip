@@ -143,7 +143,12 @@ __device__ __forceinline__ void block_first_digit(const double* h1m, const uint6
   if (lane == 0) s_wm[w] = suf;
   __syncthreads();
   uint64_t cum = suf - own;  // mass of the buckets above this thread's run
-  for (int ww = w + 1; ww < 8 * (x + 1); ++ww) cum += s_wm[ww];
+  // the totals of the view's higher waves: all 8 read at once, summed by rank
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint64_t v = s_wm[8 * x + k];
+    cum += 8 * x + k > w ? v : 0;
+  }
   const uint64_t target = s_W[x] * (uint64_t)p_num;
 #pragma unroll
   for (int u = 3; u >= 0; --u) {
@@ -186,9 +191,13 @@ __device__ __forceinline__ void block_next_digit(const uint32_t* h2c, const uint
   __syncthreads();
   uint64_t cm = mab0 + (suf_m - own_m);
   uint32_t cc = cab0 + (suf_c - own_c);
-  for (int ww = w + 1; ww < 8 * (x + 1); ++ww) {
-    cm += s_wm[ww];
-    cc += s_wc[ww];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint64_t vm = s_wm[8 * x + k];
+    const uint32_t vc = s_wc[8 * x + k];
+    const bool higher = 8 * x + k > w;
+    cm += higher ? vm : 0;
+    cc += higher ? vc : 0u;
   }
   const uint64_t target = s_W[x] * (uint64_t)p_num;
 #pragma unroll
@@ -601,29 +610,34 @@ __global__ __launch_bounds__(kDT) void k_demand(DemandArgs a, const float* __res
     {
       const uint32_t d0 = (uint32_t)s_dig[0], d1 = (uint32_t)s_dig[1];
       uint32_t above0 = 0, above1 = 0;
-      // kRingU ring loads in flight per thread before any is used
-      const float2* rk2 = reinterpret_cast<const float2*>(rk);
-      for (int64_t i0 = t; i0 < ndem; i0 += (int64_t)kRingU * kDT) {
-        float2 kk[kRingU];
+      // two tokens per 16-byte load (ndem is a multiple of the page size),
+      // kRingU loads in flight per thread before any is used
+      const float4* rk4 = reinterpret_cast<const float4*>(rk);
+      const int64_t npair = ndem >> 1;
+      auto visit = [&](uint32_t k0, uint32_t k1) {
+        above0 += (k0 >> 20) > d0;
+        above1 += (k1 >> 20) > d1;
+        if ((k0 >> 20) == d0) {
+          const int idx = atomicAdd(&s_list_n[0], 1);
+          if (idx < kListHalf) list[idx] = k0;
+        }
+        if ((k1 >> 20) == d1) {
+          const int idx = atomicAdd(&s_list_n[1], 1);
+          if (idx < kListHalf) list[kListHalf + idx] = k1;
+        }
+      };
+      for (int64_t p0 = t; p0 < npair; p0 += (int64_t)kRingU * kDT) {
+        float4 kk[kRingU];
 #pragma unroll
         for (int u = 0; u < kRingU; ++u) {
-          const int64_t i = i0 + (int64_t)u * kDT;
-          kk[u] = rk2[i < ndem ? i : i0];
+          const int64_t pi = p0 + (int64_t)u * kDT;
+          kk[u] = rk4[pi < npair ? pi : p0];
         }
 #pragma unroll
         for (int u = 0; u < kRingU; ++u) {
-          if (i0 + (int64_t)u * kDT < ndem) {
-            const uint32_t k0 = __float_as_uint(kk[u].x), k1 = __float_as_uint(kk[u].y);
-            above0 += (k0 >> 20) > d0;
-            above1 += (k1 >> 20) > d1;
-            if ((k0 >> 20) == d0) {
-              const int idx = atomicAdd(&s_list_n[0], 1);
-              if (idx < kListHalf) list[idx] = k0;
-            }
-            if ((k1 >> 20) == d1) {
-              const int idx = atomicAdd(&s_list_n[1], 1);
-              if (idx < kListHalf) list[kListHalf + idx] = k1;
-            }
+          if (p0 + (int64_t)u * kDT < npair) {
+            visit(__float_as_uint(kk[u].x), __float_as_uint(kk[u].y));
+            visit(__float_as_uint(kk[u].z), __float_as_uint(kk[u].w));
           }
         }
       }
