@@ -1,0 +1,64 @@
+"""Seeded random sweep of the boundary event on the GPU against the oracle.
+
+Each case draws a small model shape (1-3 layers, 1-2 KV heads, GQA group 4,
+optionally query-normalised), a batch of 1-6 requests with 1-20 pages each,
+per-request clusters on either summary view or none, a few free pages, a
+grant reserve, the growth policy and the method's knobs (coverage p, local
+quota, recent window), all inside what the API accepts, and compares every
+output of the event with the oracle bit for bit (the shared checker also
+compares the compacted K/V bytes and the released pages)."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_04_amd import synth
+from gpu_util import gb_config, log
+from test_gpu_tiny import check_event
+
+pytestmark = pytest.mark.gpu
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU in this container")
+
+SEEDS = list(range(32))
+
+
+def draw_case(seed: int):
+    """The case's parameters, from a generator seeded by the case number only."""
+    rng = np.random.default_rng(7000 + seed)
+    L = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 3))
+    shape = synth.ModelShape(f"rand{seed}", L=L, Hq=4 * Hkv, Hkv=Hkv, theta=1e4,
+                             qnorm=bool(rng.integers(0, 2)))
+    B = int(rng.integers(1, 7))
+    P = [int(x) for x in rng.integers(1, 21, size=B)]
+    align = [["S", "L", None][int(i)] for i in rng.integers(0, 3, size=B)]
+    sizes = [int(x) for x in rng.integers(1, 400, size=B)]
+    free = int(rng.integers(0, B + 1))
+    reserve = int(rng.integers(0, 2))
+    policy = int(rng.integers(0, 2))
+    p_num, p_den = [(99, 100), (9, 10), (1, 2), (999, 1000)][int(rng.integers(0, 4))]
+    local_quota = [0, 16, 64][int(rng.integers(0, 3))]
+    recent = [0, 16, 100][int(rng.integers(0, 3))]
+    steps = int(rng.integers(40, 160))
+    short = int(rng.integers(8, 33))
+    return dict(shape=shape, P=P, align=align, sizes=sizes, free=free, reserve=reserve,
+                policy=policy, p_num=p_num, p_den=p_den, local_quota=local_quota,
+                recent=recent, steps=steps, short=short)
+
+
+@needs_gpu
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_event(seed):
+    c = draw_case(seed)
+    s = c["shape"]
+    log(f"test_random_event[{seed}] L={s.L} Hkv={s.Hkv} qnorm={s.qnorm} P={c['P']} "
+        f"align={c['align']} free={c['free']} reserve={c['reserve']} policy={c['policy']} "
+        f"p={c['p_num']}/{c['p_den']} k_loc={c['local_quota']} R={c['recent']}")
+    B = len(c["P"])
+    pool = sum(c["P"]) + c["free"] + 3
+    wl = synth.make_workload(s, c["P"], pool, seed=9000 + seed, device="cuda",
+                             align=c["align"], cluster_sizes=c["sizes"], free_pages=c["free"],
+                             steps=c["steps"], short_steps=c["short"], max_slots=B + 2)
+    cfg = gb_config(s, max_slots=wl.max_slots, policy=c["policy"], p_num=c["p_num"],
+                    p_den=c["p_den"], local_quota=c["local_quota"], recent_window=c["recent"])
+    ref = check_event(wl, cfg, reserve=c["reserve"], check_f64=False)
+    log(f"  actions {ref['action'].tolist()} ok {ref['ok'].tolist()}")
