@@ -31,6 +31,7 @@ constexpr int kSelLdsTokens = 32768;  // candidates held in LDS (128 KiB)
 constexpr int kSelH1 = 2048;          // first radix digit: bits 30..20
 constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
 constexpr int kLoadU = 8;             // row loads in flight per thread
+constexpr int kSelList = 2048;        // boundary-bucket members kept in LDS (list path)
 static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per thread");
 
 // One radix pass's search over the whole block: thread t holds buckets
@@ -39,12 +40,14 @@ static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per threa
 // reaches nd; counts grow with the bucket, so one bucket has the crossing and
 // the thread holding it writes the extended prefix and the count below it.
 // (If no bucket reaches nd, the row has fewer than nd candidates; the top
-// bucket is taken and the caller reports the short row.)  Wave prefix sums
+// bucket is taken and the caller reports the short row.)  The bucket's own
+// count goes to s_count.  Wave prefix sums
 // by DPP, one barrier for the totals of the lower waves.
 template <int PER>
 __device__ __forceinline__ void block_select_digit(const uint32_t* hcnt, uint32_t below, int nd,
                                                    uint32_t prefix, int shift, uint32_t* s_wc,
-                                                   uint32_t& s_prefix, uint32_t& s_below) {
+                                                   uint32_t& s_prefix, uint32_t& s_below,
+                                                   uint32_t& s_count) {
   constexpr int nb = PER * kSel;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   uint32_t c[PER], own = 0;
@@ -66,9 +69,16 @@ __device__ __forceinline__ void block_select_digit(const uint32_t* hcnt, uint32_
     if ((cum >= (uint32_t)nd && before < (uint32_t)nd) || (bkt == nb - 1 && cum < (uint32_t)nd)) {
       s_prefix = prefix | ((uint32_t)bkt << shift);
       s_below = before;
+      s_count = c[u];
     }
   }
 }
+
+// Block-wide scalars of a row's selection (in LDS).
+struct SelShared {
+  uint32_t prefix, below, count;  // a digit search's result
+  int listn;                      // boundary-bucket members collected so far
+};
 
 // Steps 2-3: the nd smallest candidates of [0, nc) (skipping those marked in
 // the S_loc bitmap when PROT), written ascending to dst (and dst2); without
@@ -77,8 +87,8 @@ __device__ __forceinline__ void block_select_digit(const uint32_t* hcnt, uint32_
 template <bool PROT>
 __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc, int nd,
                                              const uint32_t* sloc, uint32_t* hcnt, int* scanbuf,
-                                             uint32_t& s_prefix, uint32_t& s_below,
-                                             int32_t* dst, int32_t* dst2, int* blkcnt) {
+                                             SelShared& sh, int32_t* dst, int32_t* dst2,
+                                             int* blkcnt) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   // step 2: value of the nd-th smallest unprotected candidate.  Three radix
   // digits: bits 30..20 (the exponent and three mantissa bits, so that the
@@ -99,12 +109,14 @@ __device__ __forceinline__ int drop_smallest(const float* __restrict__ s, int nc
     // the bucket where the count of smaller values reaches nd
     uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
     if (pass == 0)
-      block_select_digit<kSelH1 / kSel>(hcnt, below, nd, prefix, shift, s_wc, s_prefix, s_below);
+      block_select_digit<kSelH1 / kSel>(hcnt, below, nd, prefix, shift, s_wc, sh.prefix,
+                                        sh.below, sh.count);
     else
-      block_select_digit<kSelH2 / kSel>(hcnt, below, nd, prefix, shift, s_wc, s_prefix, s_below);
+      block_select_digit<kSelH2 / kSel>(hcnt, below, nd, prefix, shift, s_wc, sh.prefix,
+                                        sh.below, sh.count);
     __syncthreads();
-    prefix = s_prefix;
-    below = s_below;
+    prefix = sh.prefix;
+    below = sh.below;
     mask |= (uint32_t)(nb - 1) << shift;
     __syncthreads();
   }
@@ -235,23 +247,143 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 
 }
 
+// Steps 2-3 for a row held in LDS whose first-digit histogram (hcnt, bits
+// 30..20 of every candidate) was counted while the row was loaded, when the
+// boundary bucket of that digit holds at most kSelList candidates.  Instead
+// of further passes over the whole row: one pass marks the candidates below
+// the boundary bucket in the drop bitmap dbits (one bit per slot) and
+// collects the bucket's members into list, counting their second digit; the
+// second and third digits are resolved on list alone; the members below the
+// final value v join dbits, those equal to v go to the tie bitmap tbits.  The
+// drops are then the bits of dbits plus the `need` lowest bits of tbits
+// (ties oldest first), numbered in slot order by one block-wide prefix sum
+// over the bitmaps' words and written ascending.  Returns the number of
+// candidates selected.  Expects dbits, tbits, hist2 and sh.listn zeroed.
+__device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd, uint32_t* hcnt,
+                                                 uint32_t* hist2, int* list, uint32_t* dbits,
+                                                 uint32_t* tbits, int* scanbuf, SelShared& sh,
+                                                 uint32_t d1, uint32_t below1, int m1,
+                                                 int32_t* dst, int32_t* dst2, int* blkcnt) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
+  constexpr int kW = kSel / 64;
+  const int span = (nc + kW * 64 - 1) / (kW * 64) * 64;  // slots per wave
+  const int w0 = wv * span;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
+  hcnt[t] = 0;  // becomes the third digit's histogram (1024 buckets)
+  for (int j = 0; j < span; j += 64) {
+    const int i = w0 + j + lane;
+    const bool ok = i < nc;
+    const uint32_t key = ok ? __float_as_uint(s[i]) : 0u;
+    const uint32_t dg = (key >> 20) & (uint32_t)(kSelH1 - 1);
+    const uint64_t lo = __ballot(ok && dg < d1);
+    const bool mem = ok && dg == d1;
+    const uint64_t mm = __ballot(mem);
+    if (lo != 0 && lane < 2) dbits[((w0 + j) >> 5) + lane] = (uint32_t)(lo >> (32 * lane));
+    if (mm != 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sh.listn, __popcll(mm));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (mem) {
+        list[base + __popcll(mm & lt)] = i;
+        atomicAdd(&hist2[(key >> 10) & (uint32_t)(kSelH2 - 1)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  block_select_digit<kSelH2 / kSel>(hist2, below1, nd, d1 << 20, 10, s_wc, sh.prefix, sh.below,
+                                    sh.count);
+  __syncthreads();
+  const uint32_t p2 = sh.prefix, below2 = sh.below;
+  const uint32_t d2 = (p2 >> 10) & (uint32_t)(kSelH2 - 1);
+  for (int k = t; k < m1; k += kSel) {
+    const int i = list[k];
+    const uint32_t key = __float_as_uint(s[i]);
+    const uint32_t dg = (key >> 10) & (uint32_t)(kSelH2 - 1);
+    if (dg < d2)
+      atomicOr(&dbits[i >> 5], 1u << (i & 31));
+    else if (dg == d2)
+      atomicAdd(&hcnt[key & (uint32_t)(kSelH2 - 1)], 1u);
+  }
+  __syncthreads();
+  block_select_digit<kSelH2 / kSel>(hcnt, below2, nd, p2, 0, s_wc, sh.prefix, sh.below, sh.count);
+  __syncthreads();
+  const uint32_t v = sh.prefix;
+  const int need = nd - (int)sh.below;
+  for (int k = t; k < m1; k += kSel) {
+    const int i = list[k];
+    const uint32_t key = __float_as_uint(s[i]);
+    if ((key >> 10) == (v >> 10) && key <= v)
+      atomicOr(key < v ? &dbits[i >> 5] : &tbits[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  // word t covers slots 32 t .. 32 t + 31 (nc <= 32 kSel); one packed prefix
+  // sum gives the ties (high half) and the drops below v (low half, <= nd)
+  // in the words before this one
+  uint32_t dw = dbits[t];
+  const uint32_t tw = tbits[t];
+  const int nt = __popc(tw);
+  uint32_t tot;
+  const uint32_t ex = block_prefix_excl_u32(((uint32_t)nt << 16) | (uint32_t)__popc(dw), s_wc,
+                                            kW, tot);
+  const int ties_before = (int)(ex >> 16), lows_before = (int)(ex & 0xffffu);
+  int take = need - ties_before;
+  take = take < 0 ? 0 : (take > nt ? nt : take);
+  for (uint32_t x = tw; take > 0; --take) {  // the oldest ties of this word
+    dw |= x & (0u - x);
+    x &= x - 1;
+  }
+  const int tb = ties_before < need ? ties_before : (need > 0 ? need : 0);
+  int pos = lows_before + tb;
+  if (dw != 0) {
+    const int cnt = __popc(dw), room = nd - pos;
+    if (room > 0) atomicAdd(&blkcnt[t >> 3], cnt < room ? cnt : room);  // 8 words per page
+    for (uint32_t x = dw; x != 0 && pos < nd; x &= x - 1, ++pos) {
+      const int i = 32 * t + __builtin_ctz(x);
+      dst[pos] = i;
+      if (dst2) dst2[pos] = i;
+    }
+  }
+  const int all_ties = (int)(tot >> 16);
+  return (int)(tot & 0xffffu) + (all_ties < need ? all_ties : (need > 0 ? need : 0));
+}
+
 // One row whose importance values are at s (LDS or global memory).  The
 // b smallest candidates are found first without the block quotas; they are
 // the answer unless some block would lose more than |B_j| - min(k_loc,
 // |B_j|) of its candidates (then one of them is in that block's protected
 // top), in which case the quotas are computed and the selection repeated
 // over the unprotected candidates.  (The nd smallest of C avoid S_loc, so
-// they are also the nd smallest of C minus S_loc.)
+// they are also the nd smallest of C minus S_loc.)  With hist_ready the row
+// is in LDS with its first-digit histogram counted and the bitmaps, hist2
+// and sh.listn zeroed: the first selection then takes the list path when
+// the boundary bucket is small enough.
 __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int nd,
                                            int kloc, uint32_t* sloc, uint32_t* hcnt,
-                                           int* scanbuf, int* blkcnt, uint32_t& s_prefix,
-                                           uint32_t& s_below, int32_t* dst, int32_t* dst2,
-                                           int32_t* err) {
+                                           uint32_t* hist2, int* list, int* scanbuf, int* blkcnt,
+                                           SelShared& sh, bool hist_ready, int32_t* dst,
+                                           int32_t* dst2, int32_t* err) {
   const int t = threadIdx.x;
   for (int j = t; j < P; j += kSel) blkcnt[j] = 0;
-  __syncthreads();
-  int total = drop_smallest<false>(s, nc, nd, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
-                                   blkcnt);
+  bool listed = false;
+  if (hist_ready) {
+    block_select_digit<kSelH1 / kSel>(hcnt, 0, nd, 0, 20, reinterpret_cast<uint32_t*>(scanbuf),
+                                      sh.prefix, sh.below, sh.count);
+    __syncthreads();
+    listed = sh.count <= (uint32_t)kSelList;
+  } else {
+    __syncthreads();
+  }
+  int total;
+  if (listed) {
+    // the drop and tie bitmaps share the S_loc area (nc <= kSelLdsTokens:
+    // 1024 words each)
+    total = drop_smallest_lds(s, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
+                              scanbuf, sh, sh.prefix >> 20, sh.below, (int)sh.count, dst, dst2,
+                              blkcnt);
+  } else {
+    total = drop_smallest<false>(s, nc, nd, sloc, hcnt, scanbuf, sh, dst, dst2, blkcnt);
+  }
   __syncthreads();
   int over = 0;
   if (kloc > 0)
@@ -263,8 +395,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   if (__syncthreads_or(over)) {
     protect_blocks(s, P, nc, kloc, sloc);
     __syncthreads();
-    total = drop_smallest<true>(s, nc, nd, sloc, hcnt, scanbuf, s_prefix, s_below, dst, dst2,
-                                nullptr);
+    total = drop_smallest<true>(s, nc, nd, sloc, hcnt, scanbuf, sh, dst, dst2, nullptr);
   }
   if (t == 0 && total != nd) atomicOr(err, GP_DEVERR_SHORT);
 }
@@ -282,9 +413,11 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   __shared__ __attribute__((aligned(16))) float srow[kSelLdsTokens];
   __shared__ uint32_t sloc[kMaxRowTokens / 32];
   __shared__ uint32_t hcnt[kSelH1];
+  __shared__ uint32_t hist2[kSelH2];
+  __shared__ int list[kSelList];
   __shared__ int scanbuf[2 * (kSel / 64)];
   __shared__ int blkcnt[kMaxRowTokens / kPage];
-  __shared__ uint32_t s_prefix, s_below;
+  __shared__ SelShared sh;
   const int LH = L * Hkv;
   const int row = blockIdx.x;
   const int r = row / LH, lh = row % LH;
@@ -316,23 +449,46 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
   const int nd = m * b;  // candidates to drop
   if (nc <= kSelLdsTokens) {
-    // the row's candidates are read from HBM once, every pass runs on LDS
-    // (kLoadU loads in flight per thread before any is stored)
+    // the row's candidates are read from HBM once (kLoadU loads in flight
+    // per thread before any is stored), every pass runs on LDS; the first
+    // radix digit is counted as the values arrive
     const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
     const float4* s4 = reinterpret_cast<const float4*>(s);
-    for (int i0 = t; i0 < n4; i0 += kLoadU * kSel) {
-      float4 v[kLoadU];
+    float4 v[kLoadU];
+    auto fetch = [&](int i0) {  // indices past the row read its first entries (n4 >= 1)
 #pragma unroll
-      for (int u = 0; u < kLoadU; ++u) v[u] = s4[i0 + u * kSel < n4 ? i0 + u * kSel : i0];
+      for (int u = 0; u < kLoadU; ++u) v[u] = s4[i0 + u * kSel < n4 ? i0 + u * kSel : 0];
+    };
+    auto put = [&](int i0) {
 #pragma unroll
-      for (int u = 0; u < kLoadU; ++u)
-        if (i0 + u * kSel < n4) reinterpret_cast<float4*>(srow)[i0 + u * kSel] = v[u];
+      for (int u = 0; u < kLoadU; ++u) {
+        const int q = i0 + u * kSel;
+        if (q < n4) {
+          reinterpret_cast<float4*>(srow)[q] = v[u];
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (4 * q + c < nc) atomicAdd(&hcnt[(__float_as_uint(e[c]) >> 20) & (kSelH1 - 1)], 1u);
+        }
+      }
+    };
+    fetch(t);  // the first round in flight while the histograms are cleared
+    for (int k = t; k < kSelH1; k += kSel) hcnt[k] = 0;
+    hist2[t] = 0;
+    sloc[t] = 0;
+    sloc[t + kSel] = 0;
+    if (t == 0) sh.listn = 0;
+    __syncthreads();
+    put(t);
+    for (int i0 = t + kLoadU * kSel; i0 < n4; i0 += kLoadU * kSel) {
+      fetch(i0);
+      put(i0);
     }
     __syncthreads();
-    select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
-               dst2, err);
+    select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, true,
+               dst, dst2, err);
   } else {
-    select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, scanbuf, blkcnt, s_prefix, s_below, dst,
+    select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, false, dst,
                dst2, err);
   }
 }
