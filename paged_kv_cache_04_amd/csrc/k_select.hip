@@ -32,6 +32,7 @@ constexpr int kSelH1 = 2048;          // first radix digit: bits 30..20
 constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
 constexpr int kLoadU = 8;             // row loads in flight per thread
 constexpr int kSelList = 2048;        // boundary-bucket members kept in LDS (list path)
+static_assert(kSelLdsTokens == 4 * kLoadU * kSel, "an LDS row is one round of float4 loads");
 static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per thread");
 
 // One radix pass's search over the whole block: thread t holds buckets
@@ -247,19 +248,49 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 
 }
 
-// Steps 2-3 for a row held in LDS whose first-digit histogram (hcnt, bits
-// 30..20 of every candidate) was counted while the row was loaded, when the
-// boundary bucket of that digit holds at most kSelList candidates.  Instead
-// of further passes over the whole row: one pass marks the candidates below
-// the boundary bucket in the drop bitmap dbits (one bit per slot) and
-// collects the bucket's members into list, counting their second digit; the
-// second and third digits are resolved on list alone; the members below the
-// final value v join dbits, those equal to v go to the tie bitmap tbits.  The
-// drops are then the bits of dbits plus the `need` lowest bits of tbits
-// (ties oldest first), numbered in slot order by one block-wide prefix sum
-// over the bitmaps' words and written ascending.  Returns the number of
-// candidates selected.  Expects dbits, tbits, hist2 and sh.listn zeroed.
-__device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd, uint32_t* hcnt,
+// Drop and tie bitmaps of the list path, one bit per slot, laid out as the
+// scan reads the row: in each group of 256 slots, where lane l holds slots
+// 4 l .. 4 l + 3, word 2 c + h holds component c of lanes 32 h .. 32 h + 31.
+__device__ __forceinline__ void slot_bit(int i, int& word, uint32_t& bit) {
+  const int o = i & 255, l = o >> 2;
+  word = ((i >> 8) << 3) + ((o & 3) << 1) + (l >> 5);
+  bit = 1u << (l & 31);
+}
+
+// Bits 0..7 of x moved to bits 0, 4, .., 28.
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+
+// Slots 32 w .. 32 w + 31 of a bitmap in slot_bit's layout, as one word in
+// slot order.
+__device__ __forceinline__ uint32_t slot_word(const uint32_t* bits, int w) {
+  const int base = ((w >> 3) << 3) + ((w & 7) >> 2), sh = 8 * (w & 3);
+  uint32_t x = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) x |= spread8((bits[base + 2 * c] >> sh) & 0xffu) << c;
+  return x;
+}
+
+// Steps 2-3 for a row held in LDS and in registers (vr: thread t holds
+// candidates 4 q .. 4 q + 3 for q = t + kSel u in vr[u]) whose first-digit
+// histogram (hcnt: min(key >> 20, 2047), bits 30..20 of every finite
+// candidate) was counted while the row was loaded, when the boundary bucket
+// d1 < 2047 holds at most kSelList candidates.  Instead of further passes
+// over the whole row: one pass over the registers (each wave takes every
+// 16th 256-slot group, 4 slots per lane) marks the candidates below the boundary
+// bucket in the drop bitmap dbits and collects the bucket's members into
+// list, counting their second digit; the second and third digits are
+// resolved on list alone; the members below the final value v join dbits,
+// those equal to v go to the tie bitmap tbits.  The drops are then the bits
+// of dbits plus the `need` lowest-slot bits of tbits (ties oldest first),
+// numbered in slot order by one block-wide prefix sum over 32-slot words and
+// written ascending.  Returns the number of candidates selected.  Expects
+// dbits, tbits (1024 words each), hist2 and sh.listn zeroed.
+__device__ __forceinline__ int drop_smallest_lds(const float* s, const float4* vr, int nc, int nd,
+                                                 uint32_t* hcnt,
                                                  uint32_t* hist2, int* list, uint32_t* dbits,
                                                  uint32_t* tbits, int* scanbuf, SelShared& sh,
                                                  uint32_t d1, uint32_t below1, int m1,
@@ -267,26 +298,46 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
   constexpr int kW = kSel / 64;
-  const int span = (nc + kW * 64 - 1) / (kW * 64) * 64;  // slots per wave
-  const int w0 = wv * span;
   const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
+  // keys below a1 have a first digit below d1; members lie in [a1, a1 + 2^20)
+  const uint32_t a1 = d1 << 20;
   hcnt[t] = 0;  // becomes the third digit's histogram (1024 buckets)
-  for (int j = 0; j < span; j += 64) {
-    const int i = w0 + j + lane;
-    const bool ok = i < nc;
-    const uint32_t key = ok ? __float_as_uint(s[i]) : 0u;
-    const uint32_t dg = (key >> 20) & (uint32_t)(kSelH1 - 1);
-    const uint64_t lo = __ballot(ok && dg < d1);
-    const bool mem = ok && dg == d1;
-    const uint64_t mm = __ballot(mem);
-    if (lo != 0 && lane < 2) dbits[((w0 + j) >> 5) + lane] = (uint32_t)(lo >> (32 * lane));
-    if (mm != 0) {
+#pragma unroll
+  for (int u = 0; u < kLoadU; ++u) {
+    // vr[u] holds slots 4 q .. 4 q + 3, q = t + kSel u: group 16 u + wv of
+    // 256 slots, lane l at 4 l within it
+    const int g0 = 4 * kSel * u + 256 * wv;
+    if (g0 >= nc) break;
+    const int i0 = g0 + 4 * lane;
+    uint32_t key[4] = {__float_as_uint(vr[u].x), __float_as_uint(vr[u].y),
+                       __float_as_uint(vr[u].z), __float_as_uint(vr[u].w)};
+    if (g0 + 256 > nc) {  // the row's last group: slots past it are neither
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (i0 + c >= nc) key[c] = 0xffffffffu;
+    }
+    uint64_t lo[4], mm[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      lo[c] = __ballot(key[c] < a1);
+      mm[c] = __ballot(key[c] - a1 < (1u << 20));
+    }
+    const int g8 = g0 >> 5;  // the group's first bitmap word
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (lo[c] != 0 && lane < 2) dbits[g8 + 2 * c + lane] = (uint32_t)(lo[c] >> (32 * lane));
+    const int nm = __popcll(mm[0]) + __popcll(mm[1]) + __popcll(mm[2]) + __popcll(mm[3]);
+    if (nm != 0) {
       int base = 0;
-      if (lane == 0) base = atomicAdd(&sh.listn, __popcll(mm));
+      if (lane == 0) base = atomicAdd(&sh.listn, nm);
       base = __builtin_amdgcn_readfirstlane(base);
-      if (mem) {
-        list[base + __popcll(mm & lt)] = i;
-        atomicAdd(&hist2[(key >> 10) & (uint32_t)(kSelH2 - 1)], 1u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((mm[c] >> lane) & 1) {
+          list[base + __popcll(mm[c] & lt)] = i0 + c;
+          atomicAdd(&hist2[(key[c] >> 10) & (uint32_t)(kSelH2 - 1)], 1u);
+        }
+        base += __popcll(mm[c]);
       }
     }
   }
@@ -300,10 +351,14 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
     const int i = list[k];
     const uint32_t key = __float_as_uint(s[i]);
     const uint32_t dg = (key >> 10) & (uint32_t)(kSelH2 - 1);
-    if (dg < d2)
-      atomicOr(&dbits[i >> 5], 1u << (i & 31));
-    else if (dg == d2)
+    if (dg < d2) {
+      int w;
+      uint32_t bit;
+      slot_bit(i, w, bit);
+      atomicOr(&dbits[w], bit);
+    } else if (dg == d2) {
       atomicAdd(&hcnt[key & (uint32_t)(kSelH2 - 1)], 1u);
+    }
   }
   __syncthreads();
   block_select_digit<kSelH2 / kSel>(hcnt, below2, nd, p2, 0, s_wc, sh.prefix, sh.below, sh.count);
@@ -313,15 +368,19 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
   for (int k = t; k < m1; k += kSel) {
     const int i = list[k];
     const uint32_t key = __float_as_uint(s[i]);
-    if ((key >> 10) == (v >> 10) && key <= v)
-      atomicOr(key < v ? &dbits[i >> 5] : &tbits[i >> 5], 1u << (i & 31));
+    if ((key >> 10) == (v >> 10) && key <= v) {
+      int w;
+      uint32_t bit;
+      slot_bit(i, w, bit);
+      atomicOr(key < v ? &dbits[w] : &tbits[w], bit);
+    }
   }
   __syncthreads();
-  // word t covers slots 32 t .. 32 t + 31 (nc <= 32 kSel); one packed prefix
-  // sum gives the ties (high half) and the drops below v (low half, <= nd)
-  // in the words before this one
-  uint32_t dw = dbits[t];
-  const uint32_t tw = tbits[t];
+  // word t: slots 32 t .. 32 t + 31 in slot order (nc <= 32 kSel); one
+  // packed prefix sum gives the ties (high half) and the drops below v (low
+  // half, <= nd) in the words before this one
+  uint32_t dw = slot_word(dbits, t);
+  const uint32_t tw = slot_word(tbits, t);
   const int nt = __popc(tw);
   uint32_t tot;
   const uint32_t ex = block_prefix_excl_u32(((uint32_t)nt << 16) | (uint32_t)__popc(dw), s_wc,
@@ -355,10 +414,11 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
 // top), in which case the quotas are computed and the selection repeated
 // over the unprotected candidates.  (The nd smallest of C avoid S_loc, so
 // they are also the nd smallest of C minus S_loc.)  With hist_ready the row
-// is in LDS with its first-digit histogram counted and the bitmaps, hist2
-// and sh.listn zeroed: the first selection then takes the list path when
-// the boundary bucket is small enough.
-__device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int nd,
+// is in LDS and in the registers v, with its first-digit histogram counted
+// and the bitmaps, hist2 and sh.listn zeroed: the first selection then takes
+// the list path when the boundary bucket allows it.
+__device__ __forceinline__ void select_row(const float* __restrict__ s, const float4* v, int P,
+                                           int nc, int nd,
                                            int kloc, uint32_t* sloc, uint32_t* hcnt,
                                            uint32_t* hist2, int* list, int* scanbuf, int* blkcnt,
                                            SelShared& sh, bool hist_ready, int32_t* dst,
@@ -370,7 +430,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
     block_select_digit<kSelH1 / kSel>(hcnt, 0, nd, 0, 20, reinterpret_cast<uint32_t*>(scanbuf),
                                       sh.prefix, sh.below, sh.count);
     __syncthreads();
-    listed = sh.count <= (uint32_t)kSelList;
+    listed = sh.count <= (uint32_t)kSelList && (sh.prefix >> 20) < (uint32_t)(kSelH1 - 1);
   } else {
     __syncthreads();
   }
@@ -378,7 +438,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   if (listed) {
     // the drop and tie bitmaps share the S_loc area (nc <= kSelLdsTokens:
     // 1024 words each)
-    total = drop_smallest_lds(s, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
+    total = drop_smallest_lds(s, v, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
                               scanbuf, sh, sh.prefix >> 20, sh.below, (int)sh.count, dst, dst2,
                               blkcnt);
   } else {
@@ -449,46 +509,40 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
   const int nd = m * b;  // candidates to drop
   if (nc <= kSelLdsTokens) {
-    // the row's candidates are read from HBM once (kLoadU loads in flight
-    // per thread before any is stored), every pass runs on LDS; the first
-    // radix digit is counted as the values arrive
+    // the row's candidates are read from HBM once, all loads in flight
+    // before any is used: thread t keeps candidates 4 q .. 4 q + 3, q = t +
+    // kSel u, in v[u] and copies them to LDS, counting the first radix digit
+    // (min(key >> 20, 2047)) as they arrive
     const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
     const float4* s4 = reinterpret_cast<const float4*>(s);
     float4 v[kLoadU];
-    auto fetch = [&](int i0) {  // indices past the row read its first entries (n4 >= 1)
 #pragma unroll
-      for (int u = 0; u < kLoadU; ++u) v[u] = s4[i0 + u * kSel < n4 ? i0 + u * kSel : 0];
-    };
-    auto put = [&](int i0) {
-#pragma unroll
-      for (int u = 0; u < kLoadU; ++u) {
-        const int q = i0 + u * kSel;
-        if (q < n4) {
-          reinterpret_cast<float4*>(srow)[q] = v[u];
-          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (4 * q + c < nc) atomicAdd(&hcnt[(__float_as_uint(e[c]) >> 20) & (kSelH1 - 1)], 1u);
-        }
-      }
-    };
-    fetch(t);  // the first round in flight while the histograms are cleared
+    for (int u = 0; u < kLoadU; ++u) {  // quads past the row read its first one (n4 >= 1)
+      const int q = t + u * kSel;
+      v[u] = s4[q < n4 ? q : 0];
+    }
     for (int k = t; k < kSelH1; k += kSel) hcnt[k] = 0;
     hist2[t] = 0;
     sloc[t] = 0;
     sloc[t + kSel] = 0;
     if (t == 0) sh.listn = 0;
     __syncthreads();
-    put(t);
-    for (int i0 = t + kLoadU * kSel; i0 < n4; i0 += kLoadU * kSel) {
-      fetch(i0);
-      put(i0);
+#pragma unroll
+    for (int u = 0; u < kLoadU; ++u) {
+      const int q = t + u * kSel;
+      if (q < n4) {
+        reinterpret_cast<float4*>(srow)[q] = v[u];
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (4 * q + c < nc) atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
+      }
     }
     __syncthreads();
-    select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, true,
+    select_row(srow, v, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, true,
                dst, dst2, err);
   } else {
-    select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, false, dst,
+    select_row(s, nullptr, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, false, dst,
                dst2, err);
   }
 }
