@@ -248,139 +248,114 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 
 }
 
-// Drop and tie bitmaps of the list path, one bit per slot, laid out as the
-// scan reads the row: in each group of 256 slots, where lane l holds slots
-// 4 l .. 4 l + 3, word 2 c + h holds component c of lanes 32 h .. 32 h + 31.
-__device__ __forceinline__ void slot_bit(int i, int& word, uint32_t& bit) {
-  const int o = i & 255, l = o >> 2;
-  word = ((i >> 8) << 3) + ((o & 3) << 1) + (l >> 5);
-  bit = 1u << (l & 31);
-}
-
-// Bits 0..7 of x moved to bits 0, 4, .., 28.
-__device__ __forceinline__ uint32_t spread8(uint32_t x) {
-  x = (x | (x << 12)) & 0x000F000Fu;
-  x = (x | (x << 6)) & 0x03030303u;
-  return (x | (x << 3)) & 0x11111111u;
-}
-
-// Slots 32 w .. 32 w + 31 of a bitmap in slot_bit's layout, as one word in
-// slot order.
-__device__ __forceinline__ uint32_t slot_word(const uint32_t* bits, int w) {
-  const int base = ((w >> 3) << 3) + ((w & 7) >> 2), sh = 8 * (w & 3);
-  uint32_t x = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) x |= spread8((bits[base + 2 * c] >> sh) & 0xffu) << c;
-  return x;
-}
-
 // Steps 2-3 for a row held in LDS and in registers (vr: thread t holds
 // candidates 4 q .. 4 q + 3 for q = t + kSel u in vr[u]) whose first-digit
 // histogram (hcnt: min(key >> 20, 2047), bits 30..20 of every finite
 // candidate) was counted while the row was loaded, when the boundary bucket
-// d1 < 2047 holds at most kSelList candidates.  Instead of further passes
-// over the whole row: one pass over the registers (each wave takes every
-// 16th 256-slot group, 4 slots per lane) marks the candidates below the boundary
-// bucket in the drop bitmap dbits and collects the bucket's members into
-// list, counting their second digit; the second and third digits are
-// resolved on list alone; the members below the final value v join dbits,
-// those equal to v go to the tie bitmap tbits.  The drops are then the bits
-// of dbits plus the `need` lowest-slot bits of tbits (ties oldest first),
-// numbered in slot order by one block-wide prefix sum over 32-slot words and
-// written ascending.  Returns the number of candidates selected.  Expects
-// dbits, tbits (1024 words each), hist2 and sh.listn zeroed.
+// d1 < 2047 and the buckets below it hold at most kSelList candidates
+// together.  Instead of further passes over the whole row: one pass over the
+// registers (each wave takes every 16th 256-slot group, 4 slots per lane)
+// lists the candidates below the top of the boundary bucket (the sure drops
+// below it and the bucket's members), counting the members' second digit;
+// the second and third digits are resolved on the list alone; the listed
+// candidates below the final value v are marked in the drop bitmap dbits,
+// those equal to v in the tie bitmap tbits (bit i & 31 of word i >> 5 for
+// slot i).  The drops are then the bits of dbits plus the `need` lowest
+// bits of tbits (ties oldest first), numbered in slot order by one
+// block-wide prefix sum over the words and written ascending.  Returns the
+// number of candidates selected.  Expects dbits, tbits (1024 words each),
+// hist2 and sh.listn zeroed.
 __device__ __forceinline__ int drop_smallest_lds(const float* s, const float4* vr, int nc, int nd,
-                                                 uint32_t* hcnt,
-                                                 uint32_t* hist2, int* list, uint32_t* dbits,
-                                                 uint32_t* tbits, int* scanbuf, SelShared& sh,
-                                                 uint32_t d1, uint32_t below1, int m1,
-                                                 int32_t* dst, int32_t* dst2, int* blkcnt) {
+                                                 uint32_t* hcnt, uint32_t* hist2, int* list,
+                                                 uint32_t* dbits, uint32_t* tbits, int* scanbuf,
+                                                 SelShared& sh, uint32_t d1, uint32_t below1,
+                                                 int nl, int32_t* dst, int32_t* dst2,
+                                                 int* blkcnt) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
   constexpr int kW = kSel / 64;
-  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
-  // keys below a1 have a first digit below d1; members lie in [a1, a1 + 2^20)
-  const uint32_t a1 = d1 << 20;
+  // first digit below d1: keys below a1; the bucket's members: [a1, a2)
+  const uint32_t a1 = d1 << 20, a2 = a1 + (1u << 20);
   hcnt[t] = 0;  // becomes the third digit's histogram (1024 buckets)
-#pragma unroll
-  for (int u = 0; u < kLoadU; ++u) {
-    // vr[u] holds slots 4 q .. 4 q + 3, q = t + kSel u: group 16 u + wv of
-    // 256 slots, lane l at 4 l within it
-    const int g0 = 4 * kSel * u + 256 * wv;
-    if (g0 >= nc) break;
-    const int i0 = g0 + 4 * lane;
-    uint32_t key[4] = {__float_as_uint(vr[u].x), __float_as_uint(vr[u].y),
-                       __float_as_uint(vr[u].z), __float_as_uint(vr[u].w)};
-    if (g0 + 256 > nc) {  // the row's last group: slots past it are neither
+  // the keys of group u (vr[u]: group 16 u + wv of 256 slots, lane l at 4 l
+  // within it); slots past the row get a key above every bucket
+  auto group_keys = [&](int u, int g0, uint32_t (&key)[4]) {
+    key[0] = __float_as_uint(vr[u].x);
+    key[1] = __float_as_uint(vr[u].y);
+    key[2] = __float_as_uint(vr[u].z);
+    key[3] = __float_as_uint(vr[u].w);
+    if (g0 + 256 > nc) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if (i0 + c >= nc) key[c] = 0xffffffffu;
+        if (g0 + 4 * lane + c >= nc) key[c] = 0xffffffffu;
     }
-    uint64_t lo[4], mm[4];
+  };
+  // this wave's list entries, then its place in the list by one atomic
+  int nw = 0;
+#pragma unroll
+  for (int u = 0; u < kLoadU; ++u) {
+    const int g0 = 4 * kSel * u + 256 * wv;
+    if (g0 >= nc) break;
+    uint32_t key[4];
+    group_keys(u, g0, key);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nw += __popcll(__ballot(key[c] < a2));
+  }
+  int base = 0;
+  if (lane == 0 && nw != 0) base = atomicAdd(&sh.listn, nw);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int u = 0; u < kLoadU; ++u) {
+    const int g0 = 4 * kSel * u + 256 * wv;
+    if (g0 >= nc) break;
+    uint32_t key[4];
+    group_keys(u, g0, key);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      lo[c] = __ballot(key[c] < a1);
-      mm[c] = __ballot(key[c] - a1 < (1u << 20));
-    }
-    const int g8 = g0 >> 5;  // the group's first bitmap word
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (lo[c] != 0 && lane < 2) dbits[g8 + 2 * c + lane] = (uint32_t)(lo[c] >> (32 * lane));
-    const int nm = __popcll(mm[0]) + __popcll(mm[1]) + __popcll(mm[2]) + __popcll(mm[3]);
-    if (nm != 0) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&sh.listn, nm);
-      base = __builtin_amdgcn_readfirstlane(base);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if ((mm[c] >> lane) & 1) {
-          list[base + __popcll(mm[c] & lt)] = i0 + c;
-          atomicAdd(&hist2[(key[c] >> 10) & (uint32_t)(kSelH2 - 1)], 1u);
+      const uint64_t le = __ballot(key[c] < a2);
+      if (le != 0) {
+        if (key[c] < a2) {
+          const int rank = (int)__builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(le >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)le, 0u));
+          list[base + rank] = g0 + 4 * lane + c;
+          if (key[c] >= a1) atomicAdd(&hist2[(key[c] >> 10) & (uint32_t)(kSelH2 - 1)], 1u);
         }
-        base += __popcll(mm[c]);
+        base += __popcll(le);
       }
     }
   }
   __syncthreads();
-  block_select_digit<kSelH2 / kSel>(hist2, below1, nd, d1 << 20, 10, s_wc, sh.prefix, sh.below,
+  block_select_digit<kSelH2 / kSel>(hist2, below1, nd, a1, 10, s_wc, sh.prefix, sh.below,
                                     sh.count);
   __syncthreads();
   const uint32_t p2 = sh.prefix, below2 = sh.below;
   const uint32_t d2 = (p2 >> 10) & (uint32_t)(kSelH2 - 1);
-  for (int k = t; k < m1; k += kSel) {
+  for (int k = t; k < nl; k += kSel) {
     const int i = list[k];
     const uint32_t key = __float_as_uint(s[i]);
     const uint32_t dg = (key >> 10) & (uint32_t)(kSelH2 - 1);
-    if (dg < d2) {
-      int w;
-      uint32_t bit;
-      slot_bit(i, w, bit);
-      atomicOr(&dbits[w], bit);
-    } else if (dg == d2) {
+    if (key < a1 || dg < d2)
+      atomicOr(&dbits[i >> 5], 1u << (i & 31));
+    else if (dg == d2)
       atomicAdd(&hcnt[key & (uint32_t)(kSelH2 - 1)], 1u);
-    }
   }
   __syncthreads();
   block_select_digit<kSelH2 / kSel>(hcnt, below2, nd, p2, 0, s_wc, sh.prefix, sh.below, sh.count);
   __syncthreads();
   const uint32_t v = sh.prefix;
   const int need = nd - (int)sh.below;
-  for (int k = t; k < m1; k += kSel) {
+  for (int k = t; k < nl; k += kSel) {
     const int i = list[k];
     const uint32_t key = __float_as_uint(s[i]);
-    if ((key >> 10) == (v >> 10) && key <= v) {
-      int w;
-      uint32_t bit;
-      slot_bit(i, w, bit);
-      atomicOr(key < v ? &dbits[w] : &tbits[w], bit);
-    }
+    if ((key >> 10) == (v >> 10) && key <= v)
+      atomicOr(key < v ? &dbits[i >> 5] : &tbits[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
-  // word t: slots 32 t .. 32 t + 31 in slot order (nc <= 32 kSel); one
-  // packed prefix sum gives the ties (high half) and the drops below v (low
-  // half, <= nd) in the words before this one
-  uint32_t dw = slot_word(dbits, t);
-  const uint32_t tw = slot_word(tbits, t);
+  // word t: slots 32 t .. 32 t + 31 (nc <= 32 kSel); one packed prefix sum
+  // gives the ties (high half) and the drops below v (low half, <= nd) in
+  // the words before this one
+  uint32_t dw = dbits[t];
+  const uint32_t tw = tbits[t];
   const int nt = __popc(tw);
   uint32_t tot;
   const uint32_t ex = block_prefix_excl_u32(((uint32_t)nt << 16) | (uint32_t)__popc(dw), s_wc,
@@ -430,7 +405,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, const fl
     block_select_digit<kSelH1 / kSel>(hcnt, 0, nd, 0, 20, reinterpret_cast<uint32_t*>(scanbuf),
                                       sh.prefix, sh.below, sh.count);
     __syncthreads();
-    listed = sh.count <= (uint32_t)kSelList && (sh.prefix >> 20) < (uint32_t)(kSelH1 - 1);
+    listed = sh.below + sh.count <= (uint32_t)kSelList &&
+             (sh.prefix >> 20) < (uint32_t)(kSelH1 - 1);
   } else {
     __syncthreads();
   }
@@ -439,8 +415,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, const fl
     // the drop and tie bitmaps share the S_loc area (nc <= kSelLdsTokens:
     // 1024 words each)
     total = drop_smallest_lds(s, v, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
-                              scanbuf, sh, sh.prefix >> 20, sh.below, (int)sh.count, dst, dst2,
-                              blkcnt);
+                              scanbuf, sh, sh.prefix >> 20, sh.below,
+                              (int)(sh.below + sh.count), dst, dst2, blkcnt);
   } else {
     total = drop_smallest<false>(s, nc, nd, sloc, hcnt, scanbuf, sh, dst, dst2, blkcnt);
   }
@@ -542,8 +518,8 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
     select_row(srow, v, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, true,
                dst, dst2, err);
   } else {
-    select_row(s, nullptr, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, false, dst,
-               dst2, err);
+    select_row(s, nullptr, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
+               false, dst, dst2, err);
   }
 }
 
