@@ -11,9 +11,13 @@
 // bottom, on the row held in LDS when it fits (read from HBM once):
 //   1. the b smallest candidates of C: a 3-digit radix select (11 + 10 + 10
 //      bits) finds the value v of the b-th smallest; candidates below v are
-//      dropped and of those equal to v the oldest until exactly b (ranks in
-//      slot order from ballots over per-wave slot ranges); dropped slots
-//      written in ascending order;
+//      dropped and of those equal to v the oldest until exactly b; dropped
+//      slots written in ascending order.  For a row in LDS the first digit
+//      is counted while the row loads, and when its boundary bucket and the
+//      buckets below hold few candidates those are listed once and the
+//      later digits, the drops and the ties are taken from the list (slot
+//      order from bitmaps); otherwise each digit is a pass over the row and
+//      ranks in slot order come from ballots over per-wave slot ranges;
 //   2. if no block loses more than |B_j| - min(k_loc, |B_j|) candidates, no
 //      protected (block top-k_loc) candidate was dropped and this is Eq. 10's
 //      answer; otherwise each block's top-min(k_loc, |B_j|) is marked (one
@@ -248,13 +252,12 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 
 }
 
-// Steps 2-3 for a row held in LDS and in registers (vr: thread t holds
-// candidates 4 q .. 4 q + 3 for q = t + kSel u in vr[u]) whose first-digit
-// histogram (hcnt: min(key >> 20, 2047), bits 30..20 of every finite
-// candidate) was counted while the row was loaded, when the boundary bucket
-// d1 < 2047 and the buckets below it hold at most kSelList candidates
-// together.  Instead of further passes over the whole row: one pass over the
-// registers (each wave takes every 16th 256-slot group, 4 slots per lane)
+// Steps 2-3 for a row held in LDS whose first-digit histogram (hcnt:
+// min(key >> 20, 2047), bits 30..20 of every finite candidate) was counted
+// while the row was loaded, when the boundary bucket d1 < 2047 and the
+// buckets below it hold at most kSelList candidates together.  Instead of
+// further passes over the whole row: one pass over it (each wave takes every
+// 16th 256-slot group, 4 slots per lane)
 // lists the candidates below the top of the boundary bucket (the sure drops
 // below it and the bucket's members), counting the members' second digit;
 // the second and third digits are resolved on the list alone; the listed
@@ -265,25 +268,29 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 // block-wide prefix sum over the words and written ascending.  Returns the
 // number of candidates selected.  Expects dbits, tbits (1024 words each),
 // hist2 and sh.listn zeroed.
-__device__ __forceinline__ int drop_smallest_lds(const float* s, const float4* vr, int nc, int nd,
+__device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
                                                  uint32_t* hcnt, uint32_t* hist2, int* list,
                                                  uint32_t* dbits, uint32_t* tbits, int* scanbuf,
                                                  SelShared& sh, uint32_t d1, uint32_t below1,
                                                  int nl, int32_t* dst, int32_t* dst2,
                                                  int* blkcnt) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // in a scalar register: group
+                                                           // bounds are wave-uniform branches
   uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
   constexpr int kW = kSel / 64;
   // first digit below d1: keys below a1; the bucket's members: [a1, a2)
   const uint32_t a1 = d1 << 20, a2 = a1 + (1u << 20);
   hcnt[t] = 0;  // becomes the third digit's histogram (1024 buckets)
-  // the keys of group u (vr[u]: group 16 u + wv of 256 slots, lane l at 4 l
-  // within it); slots past the row get a key above every bucket
-  auto group_keys = [&](int u, int g0, uint32_t (&key)[4]) {
-    key[0] = __float_as_uint(vr[u].x);
-    key[1] = __float_as_uint(vr[u].y);
-    key[2] = __float_as_uint(vr[u].z);
-    key[3] = __float_as_uint(vr[u].w);
+  // the keys of this wave's group u (slots g0 .. g0 + 255, g0 = 4 kSel u +
+  // 256 wv, lane l at 4 l within it); slots past the row get a key above
+  // every bucket
+  auto group_keys = [&](int g0, uint32_t (&key)[4]) {
+    const float4 x = reinterpret_cast<const float4*>(s)[(g0 >> 2) + lane];
+    key[0] = __float_as_uint(x.x);
+    key[1] = __float_as_uint(x.y);
+    key[2] = __float_as_uint(x.z);
+    key[3] = __float_as_uint(x.w);
     if (g0 + 256 > nc) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -297,19 +304,21 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, const float4* v
     const int g0 = 4 * kSel * u + 256 * wv;
     if (g0 >= nc) break;
     uint32_t key[4];
-    group_keys(u, g0, key);
+    group_keys(g0, key);
 #pragma unroll
     for (int c = 0; c < 4; ++c) nw += __popcll(__ballot(key[c] < a2));
   }
   int base = 0;
-  if (lane == 0 && nw != 0) base = atomicAdd(&sh.listn, nw);
-  base = __builtin_amdgcn_readfirstlane(base);
+  if (nw != 0) {
+    if (lane == 0) base = atomicAdd(&sh.listn, nw);
+    base = __builtin_amdgcn_readfirstlane(base);
+  }
 #pragma unroll
   for (int u = 0; u < kLoadU; ++u) {
     const int g0 = 4 * kSel * u + 256 * wv;
     if (g0 >= nc) break;
     uint32_t key[4];
-    group_keys(u, g0, key);
+    group_keys(g0, key);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint64_t le = __ballot(key[c] < a2);
@@ -389,11 +398,10 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, const float4* v
 // top), in which case the quotas are computed and the selection repeated
 // over the unprotected candidates.  (The nd smallest of C avoid S_loc, so
 // they are also the nd smallest of C minus S_loc.)  With hist_ready the row
-// is in LDS and in the registers v, with its first-digit histogram counted
-// and the bitmaps, hist2 and sh.listn zeroed: the first selection then takes
-// the list path when the boundary bucket allows it.
-__device__ __forceinline__ void select_row(const float* __restrict__ s, const float4* v, int P,
-                                           int nc, int nd,
+// is in LDS with its first-digit histogram counted and the bitmaps, hist2
+// and sh.listn zeroed: the first selection then takes the list path when
+// the boundary bucket allows it.
+__device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int nd,
                                            int kloc, uint32_t* sloc, uint32_t* hcnt,
                                            uint32_t* hist2, int* list, int* scanbuf, int* blkcnt,
                                            SelShared& sh, bool hist_ready, int32_t* dst,
@@ -414,7 +422,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, const fl
   if (listed) {
     // the drop and tie bitmaps share the S_loc area (nc <= kSelLdsTokens:
     // 1024 words each)
-    total = drop_smallest_lds(s, v, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
+    total = drop_smallest_lds(s, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
                               scanbuf, sh, sh.prefix >> 20, sh.below,
                               (int)(sh.below + sh.count), dst, dst2, blkcnt);
   } else {
@@ -436,6 +444,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, const fl
   if (t == 0 && total != nd) atomicOr(err, GP_DEVERR_SHORT);
 }
 
+// One workgroup per row (one resident per CU by its LDS).
 __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, int kloc,
                                                  int stride,
                                                  const WsHeader* __restrict__ hdr,
@@ -479,16 +488,15 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   }
   if (flags & kReqBlocked) return;  // left uncompressed (App. E.2 page shortage)
   const int N = (int)(P * b), nc = N - R;
-  const int64_t row_tok = (int64_t)LH * off0 * b + (int64_t)lh * N;
-  const float* __restrict__ s = imp + row_tok;
+  const float* __restrict__ s = imp + (int64_t)LH * off0 * b + (int64_t)lh * N;
   int32_t* dst = dropped + (int64_t)row * stride;
   int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
   const int nd = m * b;  // candidates to drop
   if (nc <= kSelLdsTokens) {
     // the row's candidates are read from HBM once, all loads in flight
-    // before any is used: thread t keeps candidates 4 q .. 4 q + 3, q = t +
-    // kSel u, in v[u] and copies them to LDS, counting the first radix digit
-    // (min(key >> 20, 2047)) as they arrive
+    // before any is used (thread t: candidates 4 q .. 4 q + 3, q = t + kSel
+    // u, in v[u]), then copied to LDS with the first radix digit
+    // (min(key >> 20, 2047)) counted as they arrive; every pass runs on LDS
     const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
     const float4* s4 = reinterpret_cast<const float4*>(s);
     float4 v[kLoadU];
@@ -511,14 +519,15 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
         const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (4 * q + c < nc) atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
+          if (4 * q + c < nc)
+            atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
       }
     }
     __syncthreads();
-    select_row(srow, v, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh, true,
-               dst, dst2, err);
+    select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
+               true, dst, dst2, err);
   } else {
-    select_row(s, nullptr, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
+    select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
                false, dst, dst2, err);
   }
 }
