@@ -59,7 +59,7 @@ struct WsHeader {
   int32_t valid;         // 1 once the plan kernel accepted the batch
   int64_t total_tokens;  // sum of N over the batch
   int32_t row_counter;   // work queue of the demand kernel
-  int32_t pad0;
+  int32_t item_counter;  // work queue of the compaction kernel (cleared by the selection)
   int64_t pad[4];
 };
 

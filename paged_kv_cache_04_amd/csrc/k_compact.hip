@@ -16,11 +16,14 @@
 // Loads and stores are non-temporal: each byte is touched once, and keeping
 // it out of the caches leaves them to the next event's demand pass.  A
 // chunk's stores land below every later chunk's sources, and every earlier
-// chunk has finished reading, so the in-place move needs no copy of the row.  K and V rows, and different rows,
-// are disjoint items.  A persistent grid takes the items in the plan's
-// request order (longest first) with a stride of the grid; its size is a
-// context setting, so that compression on a second stream can leave CUs to
-// decoding (App. E.3).
+// chunk has finished reading, so the in-place move needs no copy of the row.
+// K and V rows, and different rows, are disjoint items.  A persistent grid
+// takes the items of the requests that compress, in the plan's request
+// order (longest first), from a queue (one atomic per item, a few µs against
+// an item's hundreds), so the rows whose first drop comes late and leave less
+// to move do not leave compute units idle at the end; its size is a context
+// setting, so that compression on a second stream can leave CUs to decoding
+// (App. E.3).
 // Prefix-preserving compression (App. E.2): a shared page i of the request
 // has a target page, and destinations in page i are written there instead.
 // Sources stay in the old pages, which are only read, so the move is still
@@ -37,13 +40,15 @@ constexpr int kPer = 16;                      // 16-byte pieces per thread per c
 constexpr int kRowsC = kCT * kPer / 16;       // destination rows per chunk (1024)
 constexpr int kMaxPages = 65536 / kPage;      // pages per row held in LDS
 static_assert(kRowsC <= kCT, "one chunk-table row per thread");
+static_assert(kMaxBatch <= kCT, "one request of the batch per thread");
 
 __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stride,
                                                  int pool_pages,
                                                  const WsHeader* __restrict__ hdr,
+                                                 int32_t* __restrict__ item_counter,
                                                  const int64_t* __restrict__ page_off,
                                                  const int32_t* __restrict__ req_order,
-                                                 int n_items,
+                                                 int B,
                                                  const int8_t* __restrict__ action,
                                                  uint16_t* __restrict__ k_pool,
                                                  uint16_t* __restrict__ v_pool,
@@ -58,10 +63,21 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
   __shared__ int32_t pgd[kMaxPages];  // destination pages
   __shared__ int64_t s_src[2][kRowsC];
   __shared__ int64_t s_dst[2][kRowsC];
-  __shared__ int bad, first_new;
+  __shared__ int32_t creq[kMaxBatch];  // requests that compress, in the plan's order
+  __shared__ uint32_t s_w[kCT / 64];
+  __shared__ int bad, first_new, s_it;
   if (!hdr->valid) return;
   const int LH = L * Hkv;
   const int t = threadIdx.x;
+  // whether request r has rows to move (the item below checks the same)
+  auto compresses = [&](int r) -> bool {
+    const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+    const int64_t P = page_off[r + 1] - page_off[r];
+    const int32_t flags = req_flags[r];
+    if (act != GP_COMPRESS && (act != GP_SHRINK || stride < 2 * b)) return false;
+    const int m = act == GP_SHRINK ? 2 : 1;
+    return P >= m + 1 && !(flags & (kReqBlocked | kReqTooLong));
+  };
   // one item: the K (which 0) or V (which 1) chain of row (r, lh); every
   // value that steers a branch is workgroup-uniform and read into a scalar
   auto item = [&](int r, int lh, int which) {
@@ -160,10 +176,26 @@ __global__ __launch_bounds__(kCT) void k_compact(int L, int Hkv, int b, int stri
       req_flags[r] = kReqCompacted;
     }
   };
-  // items in the plan's request order (longest first), 2 LH per request,
-  // taken with a stride of the grid
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int r = __builtin_amdgcn_readfirstlane(req_order[it / (2 * LH)]);
+  // the compressing requests in the plan's order (longest first), 2 LH
+  // items each, handed out one at a time by the queue
+  int r_t = -1;
+  if (t < B) {
+    r_t = req_order[t];
+    if (!compresses(r_t)) r_t = -1;
+  }
+  uint32_t n_c;
+  const uint32_t pos = block_prefix_excl_u32(r_t >= 0 ? 1u : 0u, s_w, kCT / 64, n_c);
+  if (r_t >= 0) creq[pos] = r_t;
+  __syncthreads();
+  const int n_items = 2 * LH * (int)n_c;
+  if (n_items == 0) return;
+  for (;;) {
+    if (t == 0) s_it = atomicAdd(item_counter, 1);
+    __syncthreads();
+    const int it = s_it;
+    __syncthreads();  // every thread has the item before the next one is fetched
+    if (it >= n_items) break;
+    const int r = creq[it / (2 * LH)];
     const int rem = it % (2 * LH);
     item(r, rem >> 1, rem & 1);
     __syncthreads();  // the next item rewrites the LDS tables
@@ -180,14 +212,14 @@ hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_
   hipLaunchKernelGGL(k_compact, dim3((unsigned)grid), dim3(kCT), 0, s, p.L, p.Hkv, p.b,
                      p.b * p.max_freed(), pool_pages,
                      reinterpret_cast<const WsHeader*>(base + w.header),
+                     &reinterpret_cast<WsHeader*>(base + w.header)->item_counter,
                      reinterpret_cast<const int64_t*>(base + w.page_off),
-                     reinterpret_cast<const int32_t*>(base + w.req_order), (int)n_items, action,
+                     reinterpret_cast<const int32_t*>(base + w.req_order), B, action,
                      k_pool, v_pool,
                      block_table, max_pages, num_tokens,
                      reinterpret_cast<const int32_t*>(base + w.dropped),
                      shared ? reinterpret_cast<const int32_t*>(base + w.target) : nullptr,
                      reinterpret_cast<int32_t*>(base + w.req_flags), err);
-  (void)B;
   return hipGetLastError();
 }
 

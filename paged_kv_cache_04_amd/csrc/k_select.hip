@@ -454,6 +454,7 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
                                                  int32_t* __restrict__ dropped,
                                                  int32_t* __restrict__ dropped_out,
                                                  const int32_t* __restrict__ req_flags,
+                                                 int32_t* __restrict__ item_counter,
                                                  int32_t* __restrict__ err) {
   __shared__ __attribute__((aligned(16))) float srow[kSelLdsTokens];
   __shared__ uint32_t sloc[kMaxRowTokens / 32];
@@ -466,6 +467,8 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   const int LH = L * Hkv;
   const int row = blockIdx.x;
   const int r = row / LH, lh = row % LH;
+  // the compaction that follows takes its items from this counter
+  if (row == 0 && threadIdx.x == 0) item_counter[0] = 0;
   // the row's metadata in one round of loads (all inside the workspace and
   // the caller's arrays whatever the batch), looked at after validity
   const int valid = hdr->valid;
@@ -541,7 +544,8 @@ hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t
                      reinterpret_cast<const int64_t*>(base + w.page_off), action,
                      reinterpret_cast<const float*>(base + w.imp),
                      reinterpret_cast<int32_t*>(base + w.dropped), dropped_out,
-                     reinterpret_cast<const int32_t*>(base + w.req_flags), err);
+                     reinterpret_cast<const int32_t*>(base + w.req_flags),
+                     &reinterpret_cast<WsHeader*>(base + w.header)->item_counter, err);
   (void)B;
   return hipGetLastError();
 }
