@@ -329,7 +329,8 @@ gp_status gp_compress_hold(gp_ctx* c, const gp_pool* pool, const gp_batch* bt,
     });
   if (e == hipSuccess)
     e = timed(c, GP_K_SELECT, s, [&] {
-      return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, s);
+      return gp::launch_select(p, w, c->batch, action, ws, dropped_out, c->d_err, c->num_cus,
+                               s);
     });
   if (e == hipSuccess)
     e = timed(c, GP_K_COMPACT, s, [&] {

@@ -264,7 +264,8 @@ hipError_t launch_share(const Params& p, const WsLayout& w, int B, const int8_t*
                         void* ws, int64_t* counters, int32_t* err, hipStream_t s);
 
 hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t* action,
-                         void* ws, int32_t* dropped_out, int32_t* err, hipStream_t s);
+                         void* ws, int32_t* dropped_out, int32_t* err, int num_cus,
+                         hipStream_t s);
 
 hipError_t launch_compact(const Params& p, const WsLayout& w, int B, const int8_t* action,
                           uint16_t* k_pool, uint16_t* v_pool, int pool_pages,

@@ -444,9 +444,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   if (t == 0 && total != nd) atomicOr(err, GP_DEVERR_SHORT);
 }
 
-// One workgroup per row (one resident per CU by its LDS).
+// Persistent: one workgroup per CU (its LDS allows no more), workgroup g
+// taking rows g, g + G, g + 2 G, ... of the G it runs beside; a row costs
+// no workgroup launch (16 waves and the LDS allocation) of its own.
 __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, int kloc,
-                                                 int stride,
+                                                 int stride, int nrows,
                                                  const WsHeader* __restrict__ hdr,
                                                  const int64_t* __restrict__ page_off,
                                                  const int8_t* __restrict__ action,
@@ -465,81 +467,84 @@ __global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, i
   __shared__ int blkcnt[kMaxRowTokens / kPage];
   __shared__ SelShared sh;
   const int LH = L * Hkv;
-  const int row = blockIdx.x;
-  const int r = row / LH, lh = row % LH;
-  // the compaction that follows takes its items from this counter
-  if (row == 0 && threadIdx.x == 0) item_counter[0] = 0;
-  // the row's metadata in one round of loads (all inside the workspace and
-  // the caller's arrays whatever the batch), looked at after validity
-  const int valid = hdr->valid;
-  const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
-  const int64_t off0 = page_off[r], off1 = page_off[r + 1];
-  const int32_t flags = req_flags[r];
-  if (!valid) return;
-  if (act != GP_COMPRESS && act != GP_SHRINK) return;
-  if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
-  const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
-  const int64_t P = off1 - off0;
   const int t = threadIdx.x;
-  if (flags & kReqTooLong) {  // longer than the selection takes: left as it is
-    if (t == 0 && lh == 0) atomicOr(err, GP_DEVERR_LONG);
-    return;
-  }
-  if (P < m + 1) {
-    if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
-    return;
-  }
-  if (flags & kReqBlocked) return;  // left uncompressed (App. E.2 page shortage)
-  const int N = (int)(P * b), nc = N - R;
-  const float* __restrict__ s = imp + (int64_t)LH * off0 * b + (int64_t)lh * N;
-  int32_t* dst = dropped + (int64_t)row * stride;
-  int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
-  const int nd = m * b;  // candidates to drop
-  if (nc <= kSelLdsTokens) {
-    // the row's candidates are read from HBM once, all loads in flight
-    // before any is used (thread t: candidates 4 q .. 4 q + 3, q = t + kSel
-    // u, in v[u]), then copied to LDS with the first radix digit
-    // (min(key >> 20, 2047)) counted as they arrive; every pass runs on LDS
-    const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
-    const float4* s4 = reinterpret_cast<const float4*>(s);
-    float4 v[kLoadU];
-#pragma unroll
-    for (int u = 0; u < kLoadU; ++u) {  // quads past the row read its first one (n4 >= 1)
-      const int q = t + u * kSel;
-      v[u] = s4[q < n4 ? q : 0];
+  // the compaction that follows takes its items from this counter
+  if (blockIdx.x == 0 && t == 0) item_counter[0] = 0;
+  if (!hdr->valid) return;
+  for (int row = blockIdx.x; row < nrows; row += gridDim.x) {
+    const int r = row / LH, lh = row % LH;
+    // the row's metadata in one round of loads
+    const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+    const int64_t off0 = page_off[r], off1 = page_off[r + 1];
+    const int32_t flags = req_flags[r];
+    if (act != GP_COMPRESS && act != GP_SHRINK) continue;
+    if (act == GP_SHRINK && stride < 2 * b) continue;  // Shrink outside its policy: ignored
+    const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
+    const int64_t P = off1 - off0;
+    if (flags & kReqTooLong) {  // longer than the selection takes: left as it is
+      if (t == 0 && lh == 0) atomicOr(err, GP_DEVERR_LONG);
+      continue;
     }
-    for (int k = t; k < kSelH1; k += kSel) hcnt[k] = 0;
-    hist2[t] = 0;
-    sloc[t] = 0;
-    sloc[t + kSel] = 0;
-    if (t == 0) sh.listn = 0;
-    __syncthreads();
+    if (P < m + 1) {
+      if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
+      continue;
+    }
+    if (flags & kReqBlocked) continue;  // left uncompressed (App. E.2 page shortage)
+    const int N = (int)(P * b), nc = N - R;
+    const float* __restrict__ s = imp + (int64_t)LH * off0 * b + (int64_t)lh * N;
+    int32_t* dst = dropped + (int64_t)row * stride;
+    int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
+    const int nd = m * b;  // candidates to drop
+    if (nc <= kSelLdsTokens) {
+      // the row's candidates are read from HBM once, all loads in flight
+      // before any is used (thread t: candidates 4 q .. 4 q + 3, q = t + kSel
+      // u, in v[u]), then copied to LDS with the first radix digit
+      // (min(key >> 20, 2047)) counted as they arrive; every pass runs on LDS
+      const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
+      const float4* s4 = reinterpret_cast<const float4*>(s);
+      float4 v[kLoadU];
 #pragma unroll
-    for (int u = 0; u < kLoadU; ++u) {
-      const int q = t + u * kSel;
-      if (q < n4) {
-        reinterpret_cast<float4*>(srow)[q] = v[u];
-        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (4 * q + c < nc)
-            atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
+      for (int u = 0; u < kLoadU; ++u) {  // quads past the row read its first one (n4 >= 1)
+        const int q = t + u * kSel;
+        v[u] = s4[q < n4 ? q : 0];
       }
+      for (int k = t; k < kSelH1; k += kSel) hcnt[k] = 0;
+      hist2[t] = 0;
+      sloc[t] = 0;
+      sloc[t + kSel] = 0;
+      if (t == 0) sh.listn = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kLoadU; ++u) {
+        const int q = t + u * kSel;
+        if (q < n4) {
+          reinterpret_cast<float4*>(srow)[q] = v[u];
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (4 * q + c < nc)
+              atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
+        }
+      }
+      __syncthreads();
+      select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
+                 true, dst, dst2, err);
+    } else {
+      select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
+                 false, dst, dst2, err);
     }
-    __syncthreads();
-    select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
-               true, dst, dst2, err);
-  } else {
-    select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
-               false, dst, dst2, err);
+    __syncthreads();  // this row's LDS reads done before the next row's setup
   }
 }
 
 hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t* action,
-                         void* ws, int32_t* dropped_out, int32_t* err, hipStream_t s) {
+                         void* ws, int32_t* dropped_out, int32_t* err, int num_cus,
+                         hipStream_t s) {
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(k_select, dim3((unsigned)w.rows), dim3(kSel), 0, s, p.L, p.Hkv, p.b, p.R,
-                     p.kloc, p.b * p.max_freed(),
+  const int rows = (int)w.rows;
+  const int grid = num_cus < rows ? num_cus : rows;
+  hipLaunchKernelGGL(k_select, dim3((unsigned)grid), dim3(kSel), 0, s, p.L, p.Hkv, p.b, p.R,
+                     p.kloc, p.b * p.max_freed(), rows,
                      reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), action,
                      reinterpret_cast<const float*>(base + w.imp),
