@@ -46,8 +46,8 @@ static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per threa
 // the thread holding it writes the extended prefix and the count below it.
 // (If no bucket reaches nd, the row has fewer than nd candidates; the top
 // bucket is taken and the caller reports the short row.)  The bucket's own
-// count goes to s_count.  Wave prefix sums
-// by DPP, one barrier for the totals of the lower waves.
+// count goes to s_count.  Wave prefix sums by DPP, one barrier for the
+// totals of the lower waves.
 template <int PER>
 __device__ __forceinline__ void block_select_digit(const uint32_t* hcnt, uint32_t below, int nd,
                                                    uint32_t prefix, int shift, uint32_t* s_wc,
@@ -257,9 +257,9 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 // while the row was loaded, when the boundary bucket d1 < 2047 and the
 // buckets below it hold at most kSelList candidates together.  Instead of
 // further passes over the whole row: one pass over it (each wave takes every
-// 16th 256-slot group, 4 slots per lane)
-// lists the candidates below the top of the boundary bucket (the sure drops
-// below it and the bucket's members), counting the members' second digit;
+// 16th 256-slot group, 4 slots per lane) lists the candidates below the top
+// of the boundary bucket (the sure drops below it and the bucket's members),
+// counting the members' second digit;
 // the second and third digits are resolved on the list alone; the listed
 // candidates below the final value v are marked in the drop bitmap dbits,
 // those equal to v in the tie bitmap tbits (bit i & 31 of word i >> 5 for
@@ -275,8 +275,9 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
                                                  int nl, int32_t* dst, int32_t* dst2,
                                                  int* blkcnt) {
   const int t = threadIdx.x, lane = t & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // in a scalar register: group
-                                                           // bounds are wave-uniform branches
+  // the wave index in a scalar register, so that the group bounds below are
+  // wave-uniform branches
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   uint32_t* s_wc = reinterpret_cast<uint32_t*>(scanbuf);
   constexpr int kW = kSel / 64;
   // first digit below d1: keys below a1; the bucket's members: [a1, a2)
