@@ -258,6 +258,47 @@ def test_junk_page_needs_block_quota():
 
 
 @needs_gpu
+@pytest.mark.parametrize("every,policy,action", [(7, 0, None), (4, 1, [2, 0])])
+def test_ties_spread_over_pages(every, policy, action):
+    """Every 7th (or 4th) slot of request 0 holds a key pointing away from both
+    summary directions in every (layer, KV head): those 400 (or 700) slots get
+    importance exactly 0, the row's lowest, spread thinly enough over the pages
+    that no block quota binds.  The b (or, for a caller-forced Shrink, 2b)
+    drops are the oldest of them: a selection whose ties at the threshold
+    span many 32-slot words and pages."""
+    log(f"test_ties_spread_over_pages[{every},{policy}]")
+    wl = synth.make_workload(SMALL, [12, 5], 24, seed=5150 + every, device="cuda",
+                             align=["L", "S"], cluster_sizes=[40, 40], free_pages=0, steps=120,
+                             short_steps=16, max_slots=4)
+    s = wl.shape
+    half = s.d // 2
+    pos = int(wl.position[0].item())
+    cos, sin = wl.rope[pos, :half], wl.rope[pos, half:]
+    away = synth.rotate_keys(-100.0 * (wl.u_short[0] + wl.u_long[0]), cos, sin)  # [L][Hkv][d]
+    away = away.to(torch.bfloat16)
+    cfg = gb_config(s, max_slots=wl.max_slots, policy=policy)
+    N, R = 12 * s.b, cfg.recent_window
+    n_tied = 400 if every == 7 else 700
+    slots = 5 + every * np.arange(n_tied)
+    assert slots[-1] < N - R  # candidates only (the window is kept)
+    bt = wl.block_table[0].cpu().numpy()
+    for slot in slots.tolist():
+        wl.k_pool[:, int(bt[slot // s.b]), :, slot % s.b] = away
+    ref = check_event(wl, cfg, check_f64=False, action=action)
+    nd = s.b * (2 if action else 1)
+    for (r, l, h), d in ref["dropped"].items():
+        if r != 0:
+            continue
+        # the threshold is 0 and more candidates tie there than are dropped
+        # (all the planted ones, perhaps a few more), few enough for the
+        # selection's boundary-bucket list; the drops are the oldest of them
+        imp = ref["dem"]["abar"][(r, l, h)].max(axis=1)[:N - R]
+        zero = np.nonzero(imp == 0.0)[0]
+        assert np.isin(slots, zero).all() and nd < zero.size <= 2048, (l, h, zero.size)
+        assert np.array_equal(d, zero[:nd]), (l, h, d[:4])
+
+
+@needs_gpu
 @pytest.mark.parametrize("k_loc,reserve", [(0, 0), (64, 1), (120, 0)])
 def test_quota_and_reserve(k_loc, reserve):
     """k_loc = 0 (plain top-k), the default 64, and 120 (the largest quota that
