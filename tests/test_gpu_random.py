@@ -62,3 +62,45 @@ def test_random_event(seed):
                     p_den=c["p_den"], local_quota=c["local_quota"], recent_window=c["recent"])
     ref = check_event(wl, cfg, reserve=c["reserve"], check_f64=False)
     log(f"  actions {ref['action'].tolist()} ok {ref['ok'].tolist()}")
+
+
+LONG_SEEDS = list(range(8))
+
+
+def draw_long_case(seed: int):
+    """Longer rows: 1-3 requests of 2-200 pages (rows beyond 32768 candidates
+    take the selection's HBM path), up to 8 KV heads."""
+    rng = np.random.default_rng(8000 + seed)
+    L = int(rng.integers(1, 3))
+    Hkv = [2, 4, 8][int(rng.integers(0, 3))]
+    shape = synth.ModelShape(f"long{seed}", L=L, Hq=4 * Hkv, Hkv=Hkv, theta=5e5,
+                             qnorm=bool(rng.integers(0, 2)))
+    B = int(rng.integers(1, 4))
+    P = [int(x) for x in rng.integers(2, 201, size=B)]
+    align = [["S", "L", None][int(i)] for i in rng.integers(0, 3, size=B)]
+    sizes = [int(x) for x in rng.integers(1, 2000, size=B)]
+    free = int(rng.integers(0, B + 1))
+    policy = int(rng.integers(0, 2))
+    p_num, p_den = [(99, 100), (9, 10), (1, 2)][int(rng.integers(0, 3))]
+    local_quota = [0, 64][int(rng.integers(0, 2))]
+    return dict(shape=shape, P=P, align=align, sizes=sizes, free=free, policy=policy,
+                p_num=p_num, p_den=p_den, local_quota=local_quota)
+
+
+@needs_gpu
+@pytest.mark.parametrize("seed", LONG_SEEDS)
+def test_random_event_long_rows(seed):
+    c = draw_long_case(seed)
+    s = c["shape"]
+    log(f"test_random_event_long_rows[{seed}] L={s.L} Hkv={s.Hkv} qnorm={s.qnorm} P={c['P']} "
+        f"align={c['align']} free={c['free']} policy={c['policy']} "
+        f"p={c['p_num']}/{c['p_den']} k_loc={c['local_quota']}")
+    B = len(c["P"])
+    pool = sum(c["P"]) + c["free"] + 3
+    wl = synth.make_workload(s, c["P"], pool, seed=9500 + seed, device="cuda",
+                             align=c["align"], cluster_sizes=c["sizes"], free_pages=c["free"],
+                             steps=64, short_steps=16, max_slots=B + 2)
+    cfg = gb_config(s, max_slots=wl.max_slots, policy=c["policy"], p_num=c["p_num"],
+                    p_den=c["p_den"], local_quota=c["local_quota"])
+    ref = check_event(wl, cfg, check_f64=False)
+    log(f"  actions {ref['action'].tolist()}")
