@@ -6,7 +6,8 @@ per-request clusters on either summary view or none, a few free pages, a
 grant reserve, the growth policy and the method's knobs (coverage p, local
 quota, recent window), all inside what the API accepts, and compares every
 output of the event with the oracle bit for bit (the shared checker also
-compares the compacted K/V bytes and the released pages)."""
+compares the compacted K/V bytes and the released pages).  A second set
+draws longer rows (up to 200 pages, up to 8 KV heads)."""
 import numpy as np
 import pytest
 import torch
