@@ -8,16 +8,18 @@
 // Candidates C = [0, N - R): the R newest slots are always kept.  Order:
 // larger importance first, equal importance the newer slot first.  With
 // exactly b candidates to drop per row, the selection is computed from the
-// bottom, on the row held in LDS when it fits (read from HBM once):
+// bottom:
 //   1. the b smallest candidates of C: a 3-digit radix select (11 + 10 + 10
 //      bits) finds the value v of the b-th smallest; candidates below v are
 //      dropped and of those equal to v the oldest until exactly b; dropped
-//      slots written in ascending order.  For a row in LDS the first digit
-//      is counted while the row loads, and when its boundary bucket and the
-//      buckets below hold few candidates those are listed once and the
-//      later digits, the drops and the ties are taken from the list (slot
-//      order from bitmaps); otherwise each digit is a pass over the row and
-//      ranks in slot order come from ballots over per-wave slot ranges;
+//      slots written in ascending order.  A row of up to 32768 candidates
+//      is read from HBM once into the workgroup's registers and its first
+//      digit counted as it arrives; when the boundary bucket and the
+//      buckets below hold few candidates those are listed once (slot and
+//      key) and the later digits, the drops and the ties are taken from the
+//      list (slot order from bitmaps).  Otherwise, and for longer rows, each
+//      digit is a pass over the row's importance array in HBM and ranks in
+//      slot order come from ballots over per-wave slot ranges;
 //   2. if no block loses more than |B_j| - min(k_loc, |B_j|) candidates, no
 //      protected (block top-k_loc) candidate was dropped and this is Eq. 10's
 //      answer; otherwise each block's top-min(k_loc, |B_j|) is marked (one
@@ -29,14 +31,16 @@
 
 namespace gp {
 
-constexpr int kSel = 1024;
+constexpr int kSel = 512;
 constexpr int kMaxRowTokens = 65536;
-constexpr int kSelLdsTokens = 32768;  // candidates held in LDS (128 KiB)
+constexpr int kSelRegTokens = 32768;  // candidates a workgroup holds in registers
 constexpr int kSelH1 = 2048;          // first radix digit: bits 30..20
 constexpr int kSelH2 = 1024;          // second and third digits: 10 bits each
-constexpr int kLoadU = 8;             // row loads in flight per thread
-constexpr int kSelList = 2048;        // boundary-bucket members kept in LDS (list path)
-static_assert(kSelLdsTokens == 4 * kLoadU * kSel, "an LDS row is one round of float4 loads");
+constexpr int kLoadU = 16;            // float4 row loads per thread, all in flight at once
+constexpr int kSelList = 2048;        // candidates the list path keeps (slot and key)
+constexpr int kBitWords = kSelRegTokens / 32;  // words of each list-path bitmap
+static_assert(kSelRegTokens == 4 * kLoadU * kSel, "a register row is one round of float4 loads");
+static_assert(kBitWords % kSel == 0, "whole bitmap words per thread");
 static_assert(kSelH1 % kSel == 0 && kSelH2 % kSel == 0, "whole buckets per thread");
 
 // One radix pass's search over the whole block: thread t holds buckets
@@ -252,28 +256,30 @@ __device__ __forceinline__ void protect_blocks(const float* __restrict__ s, int 
 
 }
 
-// Steps 2-3 for a row held in LDS whose first-digit histogram (hcnt:
-// min(key >> 20, 2047), bits 30..20 of every finite candidate) was counted
-// while the row was loaded, when the boundary bucket d1 < 2047 and the
+// Steps 2-3 for a row held in registers (vr: thread t holds candidates
+// 4 q .. 4 q + 3 for q = t + kSel u in vr[u]) whose first-digit histogram
+// (hcnt: min(key >> 20, 2047), bits 30..20 of every finite candidate) was
+// counted as the row arrived, when the boundary bucket d1 < 2047 and the
 // buckets below it hold at most kSelList candidates together.  Instead of
-// further passes over the whole row: one pass over it (each wave takes every
-// 16th 256-slot group, 4 slots per lane) lists the candidates below the top
-// of the boundary bucket (the sure drops below it and the bucket's members),
-// counting the members' second digit;
-// the second and third digits are resolved on the list alone; the listed
-// candidates below the final value v are marked in the drop bitmap dbits,
-// those equal to v in the tie bitmap tbits (bit i & 31 of word i >> 5 for
-// slot i).  The drops are then the bits of dbits plus the `need` lowest
+// further passes over the whole row: one pass over the registers (each wave
+// takes every kSel/64-th 256-slot group, 4 slots per lane) lists the slots
+// and keys of the candidates below the top of the boundary bucket (the sure
+// drops below it and the bucket's members), counting the members' second
+// digit; the second and third digits are resolved on the list alone; the
+// listed candidates below the final value v are marked in the drop bitmap
+// dbits, those equal to v in the tie bitmap tbits (bit i & 31 of word i >> 5
+// for slot i).  The drops are then the bits of dbits plus the `need` lowest
 // bits of tbits (ties oldest first), numbered in slot order by one
-// block-wide prefix sum over the words and written ascending.  Returns the
-// number of candidates selected.  Expects dbits, tbits (1024 words each),
-// hist2 and sh.listn zeroed.
-__device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
-                                                 uint32_t* hcnt, uint32_t* hist2, int* list,
-                                                 uint32_t* dbits, uint32_t* tbits, int* scanbuf,
-                                                 SelShared& sh, uint32_t d1, uint32_t below1,
-                                                 int nl, int32_t* dst, int32_t* dst2,
-                                                 int* blkcnt) {
+// block-wide prefix sum over the words (kBitWords / kSel consecutive words
+// per thread) and written ascending.  Returns the number of candidates
+// selected.  Expects dbits, tbits (kBitWords words each), hist2 and sh.listn
+// zeroed.
+__device__ __forceinline__ int drop_smallest_reg(const float4* vr, int nc, int nd,
+                                                 uint32_t* hcnt, uint32_t* hist2, int* lslot,
+                                                 uint32_t* lkey, uint32_t* dbits,
+                                                 uint32_t* tbits, int* scanbuf, SelShared& sh,
+                                                 uint32_t d1, uint32_t below1, int nl,
+                                                 int32_t* dst, int32_t* dst2, int* blkcnt) {
   const int t = threadIdx.x, lane = t & 63;
   // the wave index in a scalar register, so that the group bounds below are
   // wave-uniform branches
@@ -282,16 +288,14 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
   constexpr int kW = kSel / 64;
   // first digit below d1: keys below a1; the bucket's members: [a1, a2)
   const uint32_t a1 = d1 << 20, a2 = a1 + (1u << 20);
-  hcnt[t] = 0;  // becomes the third digit's histogram (1024 buckets)
-  // the keys of this wave's group u (slots g0 .. g0 + 255, g0 = 4 kSel u +
-  // 256 wv, lane l at 4 l within it); slots past the row get a key above
-  // every bucket
-  auto group_keys = [&](int g0, uint32_t (&key)[4]) {
-    const float4 x = reinterpret_cast<const float4*>(s)[(g0 >> 2) + lane];
-    key[0] = __float_as_uint(x.x);
-    key[1] = __float_as_uint(x.y);
-    key[2] = __float_as_uint(x.z);
-    key[3] = __float_as_uint(x.w);
+  for (int k = t; k < kSelH2; k += kSel) hcnt[k] = 0;  // the third digit's histogram
+  // the keys of group u (slots g0 .. g0 + 255, g0 = 4 kSel u + 256 wv, lane
+  // l at 4 l within it); slots past the row get a key above every bucket
+  auto group_keys = [&](int u, int g0, uint32_t (&key)[4]) {
+    key[0] = __float_as_uint(vr[u].x);
+    key[1] = __float_as_uint(vr[u].y);
+    key[2] = __float_as_uint(vr[u].z);
+    key[3] = __float_as_uint(vr[u].w);
     if (g0 + 256 > nc) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -305,7 +309,7 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
     const int g0 = 4 * kSel * u + 256 * wv;
     if (g0 >= nc) break;
     uint32_t key[4];
-    group_keys(g0, key);
+    group_keys(u, g0, key);
 #pragma unroll
     for (int c = 0; c < 4; ++c) nw += __popcll(__ballot(key[c] < a2));
   }
@@ -319,15 +323,17 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
     const int g0 = 4 * kSel * u + 256 * wv;
     if (g0 >= nc) break;
     uint32_t key[4];
-    group_keys(g0, key);
+    group_keys(u, g0, key);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint64_t le = __ballot(key[c] < a2);
       if (le != 0) {
         if (key[c] < a2) {
-          const int rank = (int)__builtin_amdgcn_mbcnt_hi(
-              (uint32_t)(le >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)le, 0u));
-          list[base + rank] = g0 + 4 * lane + c;
+          const int k = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                   (uint32_t)(le >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)le, 0u));
+          lslot[k] = g0 + 4 * lane + c;
+          lkey[k] = key[c];
           if (key[c] >= a1) atomicAdd(&hist2[(key[c] >> 10) & (uint32_t)(kSelH2 - 1)], 1u);
         }
         base += __popcll(le);
@@ -341,8 +347,8 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
   const uint32_t p2 = sh.prefix, below2 = sh.below;
   const uint32_t d2 = (p2 >> 10) & (uint32_t)(kSelH2 - 1);
   for (int k = t; k < nl; k += kSel) {
-    const int i = list[k];
-    const uint32_t key = __float_as_uint(s[i]);
+    const int i = lslot[k];
+    const uint32_t key = lkey[k];
     const uint32_t dg = (key >> 10) & (uint32_t)(kSelH2 - 1);
     if (key < a1 || dg < d2)
       atomicOr(&dbits[i >> 5], 1u << (i & 31));
@@ -355,62 +361,76 @@ __device__ __forceinline__ int drop_smallest_lds(const float* s, int nc, int nd,
   const uint32_t v = sh.prefix;
   const int need = nd - (int)sh.below;
   for (int k = t; k < nl; k += kSel) {
-    const int i = list[k];
-    const uint32_t key = __float_as_uint(s[i]);
+    const int i = lslot[k];
+    const uint32_t key = lkey[k];
     if ((key >> 10) == (v >> 10) && key <= v)
       atomicOr(key < v ? &dbits[i >> 5] : &tbits[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
-  // word t: slots 32 t .. 32 t + 31 (nc <= 32 kSel); one packed prefix sum
-  // gives the ties (high half) and the drops below v (low half, <= nd) in
-  // the words before this one
-  uint32_t dw = dbits[t];
-  const uint32_t tw = tbits[t];
-  const int nt = __popc(tw);
-  uint32_t tot;
-  const uint32_t ex = block_prefix_excl_u32(((uint32_t)nt << 16) | (uint32_t)__popc(dw), s_wc,
-                                            kW, tot);
-  const int ties_before = (int)(ex >> 16), lows_before = (int)(ex & 0xffffu);
-  int take = need - ties_before;
-  take = take < 0 ? 0 : (take > nt ? nt : take);
-  for (uint32_t x = tw; take > 0; --take) {  // the oldest ties of this word
-    dw |= x & (0u - x);
-    x &= x - 1;
+  // words kWp t .. kWp t + kWp - 1 (slots 32 kWp t onwards, in slot order);
+  // one packed prefix sum gives the ties (high half) and the drops below v
+  // (low half, <= nd) of the words before this thread's
+  constexpr int kWp = kBitWords / kSel;
+  uint32_t dw[kWp], tw[kWp];
+  uint32_t nt_all = 0, nl_all = 0;
+#pragma unroll
+  for (int j = 0; j < kWp; ++j) {
+    dw[j] = dbits[kWp * t + j];
+    tw[j] = tbits[kWp * t + j];
+    nt_all += __popc(tw[j]);
+    nl_all += __popc(dw[j]);
   }
-  const int tb = ties_before < need ? ties_before : (need > 0 ? need : 0);
-  int pos = lows_before + tb;
-  if (dw != 0) {
-    const int cnt = __popc(dw), room = nd - pos;
-    if (room > 0) atomicAdd(&blkcnt[t >> 3], cnt < room ? cnt : room);  // 8 words per page
-    for (uint32_t x = dw; x != 0 && pos < nd; x &= x - 1, ++pos) {
-      const int i = 32 * t + __builtin_ctz(x);
-      dst[pos] = i;
-      if (dst2) dst2[pos] = i;
+  uint32_t tot;
+  const uint32_t ex = block_prefix_excl_u32((nt_all << 16) | nl_all, s_wc, kW, tot);
+  int ties_before = (int)(ex >> 16);
+  int pos = (int)(ex & 0xffffu) + (ties_before < need ? ties_before : (need > 0 ? need : 0));
+#pragma unroll
+  for (int j = 0; j < kWp; ++j) {
+    const int nt = __popc(tw[j]);
+    int take = need - ties_before;
+    take = take < 0 ? 0 : (take > nt ? nt : take);
+    uint32_t d = dw[j];
+    for (uint32_t x = tw[j]; take > 0; --take) {  // the oldest ties of this word
+      d |= x & (0u - x);
+      x &= x - 1;
+    }
+    ties_before += nt;
+    const int w = kWp * t + j;
+    if (d != 0) {
+      const int cnt = __popc(d), room = nd - pos;
+      if (room > 0) atomicAdd(&blkcnt[w >> 3], cnt < room ? cnt : room);  // 8 words per page
+      for (uint32_t x = d; x != 0; x &= x - 1, ++pos) {
+        if (pos >= nd) continue;
+        const int i = 32 * w + __builtin_ctz(x);
+        dst[pos] = i;
+        if (dst2) dst2[pos] = i;
+      }
     }
   }
   const int all_ties = (int)(tot >> 16);
   return (int)(tot & 0xffffu) + (all_ties < need ? all_ties : (need > 0 ? need : 0));
 }
 
-// One row whose importance values are at s (LDS or global memory).  The
+// One row whose importance values are at s (global memory).  The
 // b smallest candidates are found first without the block quotas; they are
 // the answer unless some block would lose more than |B_j| - min(k_loc,
 // |B_j|) of its candidates (then one of them is in that block's protected
 // top), in which case the quotas are computed and the selection repeated
 // over the unprotected candidates.  (The nd smallest of C avoid S_loc, so
-// they are also the nd smallest of C minus S_loc.)  With hist_ready the row
-// is in LDS with its first-digit histogram counted and the bitmaps, hist2
-// and sh.listn zeroed: the first selection then takes the list path when
-// the boundary bucket allows it.
-__device__ __forceinline__ void select_row(const float* __restrict__ s, int P, int nc, int nd,
-                                           int kloc, uint32_t* sloc, uint32_t* hcnt,
-                                           uint32_t* hist2, int* list, int* scanbuf, int* blkcnt,
-                                           SelShared& sh, bool hist_ready, int32_t* dst,
-                                           int32_t* dst2, int32_t* err) {
+// they are also the nd smallest of C minus S_loc.)  With vr the row is
+// also in registers with its first-digit histogram counted and the bitmaps,
+// hist2 and sh.listn zeroed: the first selection then takes the list path
+// when the boundary bucket allows it.
+__device__ __forceinline__ void select_row(const float* __restrict__ s, const float4* vr, int P,
+                                           int nc, int nd, int kloc, uint32_t* sloc,
+                                           uint32_t* hcnt, uint32_t* hist2, int* lslot,
+                                           uint32_t* lkey, int* scanbuf, int* blkcnt,
+                                           SelShared& sh, int32_t* dst, int32_t* dst2,
+                                           int32_t* err) {
   const int t = threadIdx.x;
   for (int j = t; j < P; j += kSel) blkcnt[j] = 0;
   bool listed = false;
-  if (hist_ready) {
+  if (vr) {
     block_select_digit<kSelH1 / kSel>(hcnt, 0, nd, 0, 20, reinterpret_cast<uint32_t*>(scanbuf),
                                       sh.prefix, sh.below, sh.count);
     __syncthreads();
@@ -421,9 +441,9 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   }
   int total;
   if (listed) {
-    // the drop and tie bitmaps share the S_loc area (nc <= kSelLdsTokens:
-    // 1024 words each)
-    total = drop_smallest_lds(s, nc, nd, hcnt, hist2, list, sloc, sloc + kSelLdsTokens / 32,
+    // the drop and tie bitmaps share the S_loc area (nc <= kSelRegTokens:
+    // kBitWords words each)
+    total = drop_smallest_reg(vr, nc, nd, hcnt, hist2, lslot, lkey, sloc, sloc + kBitWords,
                               scanbuf, sh, sh.prefix >> 20, sh.below,
                               (int)(sh.below + sh.count), dst, dst2, blkcnt);
   } else {
@@ -445,96 +465,92 @@ __device__ __forceinline__ void select_row(const float* __restrict__ s, int P, i
   if (t == 0 && total != nd) atomicOr(err, GP_DEVERR_SHORT);
 }
 
-// Persistent: one workgroup per CU (its LDS allows no more), workgroup g
-// taking rows g, g + G, g + 2 G, ... of the G it runs beside; a row costs
-// no workgroup launch (16 waves and the LDS allocation) of its own.
-__global__ __launch_bounds__(kSel) void k_select(int L, int Hkv, int b, int R, int kloc,
-                                                 int stride, int nrows,
-                                                 const WsHeader* __restrict__ hdr,
-                                                 const int64_t* __restrict__ page_off,
-                                                 const int8_t* __restrict__ action,
-                                                 const float* __restrict__ imp,
-                                                 int32_t* __restrict__ dropped,
-                                                 int32_t* __restrict__ dropped_out,
-                                                 const int32_t* __restrict__ req_flags,
-                                                 int32_t* __restrict__ item_counter,
-                                                 int32_t* __restrict__ err) {
-  __shared__ __attribute__((aligned(16))) float srow[kSelLdsTokens];
+// One 512-thread workgroup per row; two fit per CU (registers), so one
+// row's load is in flight while the other row is selected.
+__global__ __launch_bounds__(kSel, 2) void k_select(int L, int Hkv, int b, int R, int kloc,
+                                                    int stride,
+                                                    const WsHeader* __restrict__ hdr,
+                                                    const int64_t* __restrict__ page_off,
+                                                    const int8_t* __restrict__ action,
+                                                    const float* __restrict__ imp,
+                                                    int32_t* __restrict__ dropped,
+                                                    int32_t* __restrict__ dropped_out,
+                                                    const int32_t* __restrict__ req_flags,
+                                                    int32_t* __restrict__ item_counter,
+                                                    int32_t* __restrict__ err) {
   __shared__ uint32_t sloc[kMaxRowTokens / 32];
   __shared__ uint32_t hcnt[kSelH1];
   __shared__ uint32_t hist2[kSelH2];
-  __shared__ int list[kSelList];
+  __shared__ int lslot[kSelList];
+  __shared__ uint32_t lkey[kSelList];
   __shared__ int scanbuf[2 * (kSel / 64)];
   __shared__ int blkcnt[kMaxRowTokens / kPage];
   __shared__ SelShared sh;
   const int LH = L * Hkv;
-  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  const int r = row / LH, lh = row % LH;
   // the compaction that follows takes its items from this counter
-  if (blockIdx.x == 0 && t == 0) item_counter[0] = 0;
-  if (!hdr->valid) return;
-  for (int row = blockIdx.x; row < nrows; row += gridDim.x) {
-    const int r = row / LH, lh = row % LH;
-    // the row's metadata in one round of loads
-    const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
-    const int64_t off0 = page_off[r], off1 = page_off[r + 1];
-    const int32_t flags = req_flags[r];
-    if (act != GP_COMPRESS && act != GP_SHRINK) continue;
-    if (act == GP_SHRINK && stride < 2 * b) continue;  // Shrink outside its policy: ignored
-    const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
-    const int64_t P = off1 - off0;
-    if (flags & kReqTooLong) {  // longer than the selection takes: left as it is
-      if (t == 0 && lh == 0) atomicOr(err, GP_DEVERR_LONG);
-      continue;
-    }
-    if (P < m + 1) {
-      if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
-      continue;
-    }
-    if (flags & kReqBlocked) continue;  // left uncompressed (App. E.2 page shortage)
-    const int N = (int)(P * b), nc = N - R;
-    const float* __restrict__ s = imp + (int64_t)LH * off0 * b + (int64_t)lh * N;
-    int32_t* dst = dropped + (int64_t)row * stride;
-    int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
-    const int nd = m * b;  // candidates to drop
-    if (nc <= kSelLdsTokens) {
-      // the row's candidates are read from HBM once, all loads in flight
-      // before any is used (thread t: candidates 4 q .. 4 q + 3, q = t + kSel
-      // u, in v[u]), then copied to LDS with the first radix digit
-      // (min(key >> 20, 2047)) counted as they arrive; every pass runs on LDS
-      const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
-      const float4* s4 = reinterpret_cast<const float4*>(s);
-      float4 v[kLoadU];
+  if (row == 0 && threadIdx.x == 0) item_counter[0] = 0;
+  // the row's metadata in one round of loads (all inside the workspace and
+  // the caller's arrays whatever the batch), looked at after validity
+  const int valid = hdr->valid;
+  const int8_t act = action ? action[r] : (int8_t)GP_COMPRESS;
+  const int64_t off0 = page_off[r], off1 = page_off[r + 1];
+  const int32_t flags = req_flags[r];
+  if (!valid) return;
+  if (act != GP_COMPRESS && act != GP_SHRINK) return;
+  if (act == GP_SHRINK && stride < 2 * b) return;  // Shrink outside its policy: ignored
+  const int m = act == GP_SHRINK ? 2 : 1;  // pages of slots to free
+  const int64_t P = off1 - off0;
+  const int t = threadIdx.x;
+  if (flags & kReqTooLong) {  // longer than the selection takes: left as it is
+    if (t == 0 && lh == 0) atomicOr(err, GP_DEVERR_LONG);
+    return;
+  }
+  if (P < m + 1) {
+    if (t == 0) atomicOr(err, GP_DEVERR_SHORT);
+    return;
+  }
+  if (flags & kReqBlocked) return;  // left uncompressed (App. E.2 page shortage)
+  const int N = (int)(P * b), nc = N - R;
+  const float* __restrict__ s = imp + (int64_t)LH * off0 * b + (int64_t)lh * N;
+  int32_t* dst = dropped + (int64_t)row * stride;
+  int32_t* dst2 = dropped_out ? dropped_out + (int64_t)row * stride : nullptr;
+  const int nd = m * b;  // candidates to drop
+  if (nc <= kSelRegTokens) {
+    // the row's candidates are read from HBM once, all loads in flight
+    // before any is used (thread t: candidates 4 q .. 4 q + 3, q = t + kSel
+    // u, in v[u]), the first radix digit (min(key >> 20, 2047)) counted as
+    // they arrive
+    const int n4 = (nc + 3) / 4;  // rows start 1 KiB aligned; N is a multiple of 256
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    float4 v[kLoadU];
 #pragma unroll
-      for (int u = 0; u < kLoadU; ++u) {  // quads past the row read its first one (n4 >= 1)
-        const int q = t + u * kSel;
-        v[u] = s4[q < n4 ? q : 0];
+    for (int u = 0; u < kLoadU; ++u) {  // quads past the row read its first one (n4 >= 1)
+      const int q = t + u * kSel;
+      v[u] = s4[q < n4 ? q : 0];
+    }
+    for (int k = t; k < kSelH1; k += kSel) hcnt[k] = 0;
+    for (int k = t; k < kSelH2; k += kSel) hist2[k] = 0;
+    for (int k = t; k < 2 * kBitWords; k += kSel) sloc[k] = 0;
+    if (t == 0) sh.listn = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kLoadU; ++u) {
+      const int q = t + u * kSel;
+      if (q < n4) {
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (4 * q + c < nc) atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
       }
-      for (int k = t; k < kSelH1; k += kSel) hcnt[k] = 0;
-      hist2[t] = 0;
-      sloc[t] = 0;
-      sloc[t + kSel] = 0;
-      if (t == 0) sh.listn = 0;
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < kLoadU; ++u) {
-        const int q = t + u * kSel;
-        if (q < n4) {
-          reinterpret_cast<float4*>(srow)[q] = v[u];
-          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (4 * q + c < nc)
-              atomicAdd(&hcnt[min(__float_as_uint(e[c]) >> 20, kSelH1 - 1u)], 1u);
-        }
-      }
-      __syncthreads();
-      select_row(srow, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
-                 true, dst, dst2, err);
-    } else {
-      select_row(s, (int)P, nc, nd, kloc, sloc, hcnt, hist2, list, scanbuf, blkcnt, sh,
-                 false, dst, dst2, err);
     }
-    __syncthreads();  // this row's LDS reads done before the next row's setup
+    __syncthreads();
+    select_row(s, v, (int)P, nc, nd, kloc, sloc, hcnt, hist2, lslot, lkey, scanbuf, blkcnt, sh,
+               dst, dst2, err);
+  } else {
+    select_row(s, nullptr, (int)P, nc, nd, kloc, sloc, hcnt, hist2, lslot, lkey, scanbuf, blkcnt,
+               sh, dst, dst2, err);
   }
 }
 
@@ -542,10 +558,9 @@ hipError_t launch_select(const Params& p, const WsLayout& w, int B, const int8_t
                          void* ws, int32_t* dropped_out, int32_t* err, int num_cus,
                          hipStream_t s) {
   char* base = static_cast<char*>(ws);
-  const int rows = (int)w.rows;
-  const int grid = num_cus < rows ? num_cus : rows;
-  hipLaunchKernelGGL(k_select, dim3((unsigned)grid), dim3(kSel), 0, s, p.L, p.Hkv, p.b, p.R,
-                     p.kloc, p.b * p.max_freed(), rows,
+  (void)num_cus;
+  hipLaunchKernelGGL(k_select, dim3((unsigned)w.rows), dim3(kSel), 0, s, p.L, p.Hkv, p.b, p.R,
+                     p.kloc, p.b * p.max_freed(),
                      reinterpret_cast<const WsHeader*>(base + w.header),
                      reinterpret_cast<const int64_t*>(base + w.page_off), action,
                      reinterpret_cast<const float*>(base + w.imp),
